@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the weight-absorbed MLA path on one MI355X.
+
+A step is one pass of the whole hot path over one batch: mla_cache_write of
+the new row of every sequence (position cache_lens - 1) followed by
+mla_decode over rows 0 .. cache_lens - 1 (dense, ragged or top-k).  Inputs are
+seeded synthetic tensors with the workload's shapes; they are resident in
+HBM before timing starts.  R replicas of every input rotate from step to step
+so that the working set exceeds the 256 MB Infinity Cache (consecutive layers
+of a real model do not share weights or caches either).
+
+Timing: each replica's step is captured once in a HIP graph; the timed region
+replays K steps, bracketed by torch.cuda.synchronize().  Per-kernel durations
+come from a second pass of K eager steps with HIP events recorded around
+every kernel on the library's stream (the queue is pre-filled behind a fixed
+GPU sleep so the events time the kernels, not host launch latency).  The
+dominant kernel's average duration gives the roofline entry.  The CPU
+baseline times the oracle on a bounded sample of the same workload.
+
+Prints one JSON line.
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+MALL_BYTES = 256 << 20
+METRIC = "MLA decode tokens/s + latent-cache HBM GB/s (% of peak), H=128, T=4K–64K"
+KERNELS = ["cache_write", "absorb", "attention", "combine", "uproj"]
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            evs.append(e.value)
+        return evs
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def workload_bytes_flops(w, lens, k):
+    """Algorithmic bytes and FLOPs per kernel launch (one step)."""
+    B, H = w.batch, w.heads
+    rows = [min(k, int(n)) if k else int(n) for n in lens]
+    row_bytes = (512 + 16 + 128) if w.fp8 else (1024 + 128)
+    n_rows = sum(rows)
+    proj_w = 2 * H * 128 * 512
+    out = {
+        "absorb": (proj_w + 2 * B * H * 128, 2 * B * H * 128 * 512),
+        "attention": (n_rows * row_bytes + 2 * B * H * 64 + 4 * B + 4 * B * k,
+                      n_rows * H * 2 * (576 + 512)),
+        "combine": (0, 0),
+        "uproj": (proj_w + 2 * B * H * 128, 2 * B * H * 128 * 512),
+        "cache_write": (B * 2 * 576 + B * row_bytes + 4 * B, 0),
+    }
+    total_bytes = (2 * B * H * 192 + 2 * proj_w + n_rows * row_bytes + 4 * B + 4 * B * k
+                   + 2 * B * H * 128)
+    total_flops = 4 * B * H * 128 * 512 + n_rows * H * 2 * (576 + 512)
+    return out, total_bytes, total_flops, n_rows, row_bytes
+
+
+def build_replicas(w, x, R, mla, torch):
+    dev = "cuda:0"
+    B, T = w.batch, w.max_seq_len
+    lens = x["cache_lens"]
+    start = torch.clamp(lens - 1, min=0)
+    rows = start.long()
+    kv_new = x["kv"][torch.arange(B), rows].reshape(B, 1, 512).contiguous()
+    pe_new = x["pe"][torch.arange(B), rows].reshape(B, 1, 64).contiguous()
+    base = {
+        "q_nope": x["q_nope"].to(dev), "q_pe": x["q_pe"].to(dev), "wkv_b": x["wkv_b"].to(dev),
+        "kv_new": kv_new.to(dev), "pe_new": pe_new.to(dev),
+    }
+    if w.fp8:
+        base["kv"] = torch.zeros(B, T, 512, dtype=torch.uint8, device=dev)
+        base["scale"] = torch.zeros(B, T, 4, dtype=torch.float32, device=dev)
+        base["pe"] = torch.zeros(B, T, 64, dtype=torch.bfloat16, device=dev)
+        mla.cache_write(x["kv"].to(dev), x["pe"].to(dev), torch.zeros(B, dtype=torch.int32, device=dev),
+                        base["kv"], base["pe"], kv_scale=base["scale"])
+    else:
+        base["kv"] = x["kv"].to(dev)
+        base["scale"] = None
+        base["pe"] = x["pe"].to(dev)
+    shared = {"lens": lens.to(dev), "start": start.to(torch.int32).to(dev),
+              "topk": None if x["topk_idx"] is None else x["topk_idx"].to(dev)}
+    reps = [base]
+    for _ in range(R - 1):
+        reps.append({k: (None if v is None else v.clone()) for k, v in base.items()})
+    torch.cuda.synchronize()
+    return reps, shared
+
+
+def step(mla, r, s, out, ws, trace=None):
+    mla.cache_write(r["kv_new"], r["pe_new"], s["start"], r["kv"], r["pe"], kv_scale=r["scale"],
+                    trace_events=None if trace is None else trace[0])
+    mla.decode(r["q_nope"], r["q_pe"], r["wkv_b"], r["kv"], r["pe"], s["lens"], kv_scale=r["scale"],
+               topk_idx=s["topk"], out=out, workspace=ws,
+               trace_events=None if trace is None else trace[1])
+
+
+def cpu_baseline(w, x, seconds, oracle, synth, np, torch):
+    """The oracle, as it stands, on a bounded sample of the workload."""
+    if w.fp8:
+        kv, sc, pe = oracle.cache_write(x["kv"], x["pe"], torch.zeros(w.batch, dtype=torch.int32),
+                                        w.max_seq_len, True)
+    else:
+        kv, sc, pe = x["kv"], None, x["pe"]
+    total_pairs = w.batch * w.heads
+    pairs_all = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    done, t0 = 0, time.perf_counter()
+    chunk = max(1, min(total_pairs, 4 * oracle.num_threads()))
+    i = 0
+    while True:
+        sel = [pairs_all[(i + j) % total_pairs] for j in range(chunk)]
+        oracle.decode(x["q_nope"], x["q_pe"], x["wkv_b"], kv, pe, x["cache_lens"],
+                      synth.SOFTMAX_SCALE, kv_scale=sc, topk_idx=x["topk_idx"], pairs=sel)
+        done += chunk
+        i += chunk
+        el = time.perf_counter() - t0
+        if el >= seconds and done >= min(total_pairs, chunk):
+            break
+    steps = done / total_pairs
+    return {"value": w.batch * steps / el, "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{done} (sequence, head) outputs of {w.name} in {el:.1f} s "
+                      f"({steps:.3f} full steps; tokens/s = B x steps / time)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="dense_b1_h128_t4096")
+    ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed the MALL")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--eager", action="store_true", help="time eager launches, not graph replay")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the decode path runs on one GPU; see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mla_latent_kv_08_amd import mla, synth
+
+    w = synth.WORKLOADS[args.workload]
+    x = synth.make_inputs(w)
+    k = w.topk
+    per_kernel, total_bytes, total_flops, n_rows, row_bytes = workload_bytes_flops(
+        w, x["cache_lens"].tolist(), k)
+    working = total_bytes + 2 * w.batch * w.heads * 128
+    R = args.replicas or max(1, min(32, math.ceil(2 * MALL_BYTES / working)))
+    reps, shared = build_replicas(w, x, R, mla, torch)
+    B, H = w.batch, w.heads
+    out = torch.empty(B, 1, H, 128, dtype=torch.bfloat16, device="cuda:0")
+    p = mla.make_params(B, H, w.max_seq_len, 1 if w.fp8 else 0, topk=k)
+    ws = torch.empty(mla.decode_workspace_size(p), dtype=torch.uint8, device="cuda:0")
+
+    for i in range(args.warmup):
+        step(mla, reps[i % R], shared, out, ws)
+    torch.cuda.synchronize()
+
+    graphs = []
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(mla, reps[0], shared, out, ws)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(mla, reps[r], shared, out, ws)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+
+    # ---- timed region: exactly K steps
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if graphs:
+        for i in range(args.steps):
+            graphs[i % R].replay()
+    else:
+        for i in range(args.steps):
+            step(mla, reps[i % R], shared, out, ws)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = 1e3 * elapsed / args.steps
+
+    # ---- per-kernel durations: eager steps with HIP events around every kernel
+    hev = HipEvents()
+    ev = hev.create(10 * args.steps)
+    traces = []
+    for i in range(args.steps):
+        e = ev[10 * i: 10 * i + 10]
+        traces.append(((ctypes.c_void_p * 2)(*e[:2]), (ctypes.c_void_p * 8)(*e[2:])))
+    torch.cuda._sleep(int(2e8))  # hold the queue while the host enqueues the steps
+    for i in range(args.steps):
+        step(mla, reps[i % R], shared, out, ws,
+             trace=(ctypes.addressof(traces[i][0]), ctypes.addressof(traces[i][1])))
+    torch.cuda.synchronize()
+    dur = {kname: [] for kname in KERNELS}
+    for i in range(args.steps):
+        e = ev[10 * i: 10 * i + 10]
+        dur["cache_write"].append(hev.elapsed_ms(e[0], e[1]))
+        for j, kname in enumerate(KERNELS[1:]):
+            dur[kname].append(hev.elapsed_ms(e[2 + 2 * j], e[3 + 2 * j]))
+    hev.destroy(ev)
+    avg_us = {kname: 1e3 * float(np.mean(v)) for kname, v in dur.items()}
+    dom = max(avg_us, key=avg_us.get)
+    kb, kf = per_kernel[dom]
+    t_dom = avg_us[dom] * 1e-6
+    hbm_time, mfma_time = kb / (PEAK_HBM_GBS * 1e9), kf / (PEAK_BF16_TFLOPS * 1e12)
+    if hbm_time >= mfma_time:
+        roof = {"bound": "hbm", "achieved": kb / t_dom / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": kf / t_dom / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["avg_us"] = avg_us[dom]
+
+    tokens_per_s = B * args.steps / elapsed
+    step_s = ms_per_step * 1e-3
+    latent_bytes = n_rows * row_bytes
+    result = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": B, "heads": H, "max_seq_len": w.max_seq_len,
+            "kv_cache": "fp8_e4m3_block128" if w.fp8 else "bf16",
+            "selection": (f"top-{k}" if k else ("ragged U{%d..%d}" % w.ragged if w.ragged else "dense")),
+            "rows_per_step": n_rows, "replicas": R,
+            "launch": "eager" if args.eager else "hip graph replay",
+        },
+        "latent_cache_gbps": latent_bytes / step_s / 1e9,
+        "step_hbm_gbps": total_bytes / step_s / 1e9,
+        "step_hbm_frac": total_bytes / step_s / 1e9 / PEAK_HBM_GBS,
+        "step_mfma_frac": total_flops / step_s / 1e12 / PEAK_BF16_TFLOPS,
+        "kernel_avg_us": avg_us,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        result["cpu_baseline"] = cpu_baseline(w, x, args.cpu_seconds, oracle, synth, np, torch)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,174 @@
+/*
+ * mla.h -- C ABI of the MI355X (gfx950) weight-absorbed MLA decode library.
+ *
+ * The operation is Multi-Head Latent Attention decode in its weight-absorbed
+ * ("MQA decode") form over a compressed KV cache, as described on the pages
+ * "DeepSeek-V3.2-Exp . KV cache" (decode view: the cache-write excerpt and the
+ * "MQA decode" excerpt) and "DeepSeek MLA Architecture: How Multi-Head Latent
+ * Attention Cuts KV Cache by 93%" (section 3, decoupled RoPE; section 4, the
+ * absorption identities).  Each cached position holds a 512-wide normalised
+ * latent c_KV and a 64-wide rotary key k_R shared by all heads.
+ *
+ * Conventions for every entry point
+ *  - Tensor arguments are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or keeps them.  bf16 tensors are raw 16-bit
+ *    patterns.  All tensors are dense row-major with the shapes given below.
+ *    Pointers to bf16/uint8 tensors must be 16-byte aligned; int32/fp32
+ *    tensors 4-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *    work is enqueued asynchronously on it; no call synchronises the device,
+ *    calls hipMalloc/hipMemset, or blocks the host.  The calls are safe to
+ *    record into a HIP graph.
+ *  - Host-side argument checks run before any HIP call; on failure nothing is
+ *    enqueued and the status says why (mla_last_error() gives a detail text
+ *    for the calling thread).  A launch failure returns MLA_ERR_HIP.
+ *  - Calls from several host threads are safe; calls that write the same
+ *    buffers must be ordered by the caller (same stream or events).
+ */
+#ifndef MLA_H
+#define MLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_ABI_VERSION 1
+
+/* Fixed widths of the DeepSeek-V3 MLA layer (checked in mla_params). */
+#define MLA_KV_LORA_RANK 512 /* latent width C */
+#define MLA_QK_ROPE_DIM 64   /* rotary key width R */
+#define MLA_QK_NOPE_DIM 128  /* per-head non-rotary query/key width Dn */
+#define MLA_V_HEAD_DIM 128   /* per-head value width Dv */
+#define MLA_FP8_BLOCK 128    /* latent elements per FP8 scale */
+#define MLA_MAX_HEADS 128
+
+typedef enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size or dimension */
+  MLA_ERR_UNSUPPORTED = 2, /* a valid request this build does not implement */
+  MLA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  MLA_ERR_HIP = 4          /* the HIP runtime reported an error */
+} mla_status;
+
+typedef enum mla_kv_dtype {
+  MLA_KV_BF16 = 0,         /* latent cache holds bf16 values */
+  MLA_KV_FP8_E4M3_B128 = 1 /* latent cache holds OCP E4M3FN codes, one fp32
+                              scale per 128 contiguous latent elements */
+} mla_kv_dtype;
+
+/*
+ * Problem description, passed by pointer (host memory, read during the call).
+ *   batch         B >= 0 sequences (B == 0 is a no-op)
+ *   seqlen_q      s: new rows per sequence for mla_cache_write (>= 0);
+ *                 must be 1 for mla_decode (one query token per sequence)
+ *   num_heads     H, 1..128 (the local heads of this GPU)
+ *   max_seq_len   T: second dimension of every cache buffer, >= 1
+ *   kv_lora_rank, qk_nope_dim, qk_rope_dim, v_head_dim: must be 512, 128, 64, 128
+ *   kv_dtype      an mla_kv_dtype
+ *   topk          0: dense attention over [0, cache_lens[b]);
+ *                 k > 0: entries per sequence of topk_idx (k <= T)
+ *   softmax_scale multiplier of the logits, finite and > 0 (1/sqrt(192) for
+ *                 DeepSeek-V3; a YaRN correction is folded in by the caller)
+ *   trace_events  optional instrumentation, normally NULL.  Otherwise an array
+ *                 of hipEvent_t (as void*): mla_decode records events[2k] and
+ *                 events[2k+1] on `stream` around its k-th kernel
+ *                 (k = 0 absorb, 1 attention, 2 combine, 3 up-projection;
+ *                 8 events); mla_cache_write records events[0] and events[1]
+ *                 around its kernel.
+ */
+typedef struct mla_params {
+  int32_t batch;
+  int32_t seqlen_q;
+  int32_t num_heads;
+  int32_t max_seq_len;
+  int32_t kv_lora_rank;
+  int32_t qk_nope_dim;
+  int32_t qk_rope_dim;
+  int32_t v_head_dim;
+  int32_t kv_dtype;
+  int32_t topk;
+  float softmax_scale;
+  int32_t reserved;
+  void* const* trace_events;
+} mla_params;
+
+/*
+ * mla_cache_write -- store new rows in the latent and rotary caches.
+ *
+ * Follows the cache-write excerpt of "DeepSeek-V3.2-Exp . KV cache": rows
+ * [start_pos, start_pos + s) of each sequence receive the new latent and
+ * rotary rows.  With MLA_KV_FP8_E4M3_B128 the latent is stored in the form the
+ * page says deployment uses: per block of 128 contiguous latent elements,
+ *   scale = max|x| / 448            (fp32, IEEE division)
+ *   code  = E4M3FN(x / scale)       (fp32 IEEE division, round to nearest
+ *                                    even, saturating to +-448, sign of zero
+ *                                    kept; a block with scale 0 gets code 0)
+ * and the page's decode-side value is bf16(float(code) * scale).
+ *
+ *   kv_new     bf16 [B][s][512]
+ *   pe_new     bf16 [B][s][64]
+ *   start_pos  int32 [B] (device)
+ *   kv_cache   bf16 [>=B][T][512], or uint8 E4M3FN codes [>=B][T][512]
+ *   kv_scale   fp32 [>=B][T][4] for the FP8 cache; must be NULL for bf16
+ *   pe_cache   bf16 [>=B][T][64]
+ * Rows whose index falls outside [0, T) are dropped (nothing is stored).
+ */
+mla_status mla_cache_write(const mla_params* p, const void* kv_new, const void* pe_new,
+                           const int32_t* start_pos, void* kv_cache, float* kv_scale,
+                           void* pe_cache, void* stream);
+
+/*
+ * mla_decode_workspace_size -- bytes of device workspace mla_decode needs for
+ * these parameters (a pure host computation; no device is touched).
+ */
+mla_status mla_decode_workspace_size(const mla_params* p, size_t* bytes);
+
+/*
+ * mla_decode -- one decode step of weight-absorbed MLA for every sequence.
+ *
+ * Follows the "MQA decode" excerpt of "DeepSeek-V3.2-Exp . KV cache" and
+ * sections 3-4 of the MLA article, per sequence b and head h:
+ *   1. absorb:  qa[c]   = sum_d q_nope[b,0,h,d] * wkv_b[h,d,c]          (d < 128)
+ *   2. score:   S[t]    = (qa . c_KV[b,t] + q_pe[b,0,h] . k_R[b,t]) * softmax_scale
+ *   3. softmax over the selected positions t (dense: t < end_b; top-k: the
+ *      set of entries of topk_idx[b] inside [0, end_b))
+ *   4. reduce:  o[c]    = sum_t p[t] * c_KV[b,t,c]
+ *   5. up-project: out[b,0,h,d] = sum_c o[c] * wkv_b[h,128+d,c]
+ * with end_b = min(max(cache_lens[b], 0), T).  c_KV is the bf16 latent, or for
+ * the FP8 cache bf16(float(code) * scale).
+ *
+ *   q_nope     bf16 [B][1][H][128]
+ *   q_pe       bf16 [B][1][H][64] (already rotated)
+ *   wkv_b      bf16 [H][256][512]: rows 0..127 the key half W_UK, rows
+ *              128..255 the value half W_UV of each head
+ *   kv_cache, kv_scale, pe_cache: as for mla_cache_write
+ *   cache_lens int32 [B] (device): rows 0..cache_lens[b]-1 are valid
+ *   topk_idx   int32 [B][1][topk] (device) when topk > 0, else NULL.  Entries
+ *              outside [0, end_b) (e.g. -1 padding) are skipped; the valid
+ *              entries of a row must be distinct.
+ *   out        bf16 [B][1][H][128]
+ *   workspace  device scratch of at least mla_decode_workspace_size() bytes,
+ *              16-byte aligned; its contents are undefined after the call.
+ * A sequence with no selected position gets an output row of zeros.
+ */
+mla_status mla_decode(const mla_params* p, const void* q_nope, const void* q_pe,
+                      const void* wkv_b, const void* kv_cache, const float* kv_scale,
+                      const void* pe_cache, const int32_t* cache_lens, const int32_t* topk_idx,
+                      void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* mla_status_string(mla_status s);
+
+/* Detail text of the last failing call on the calling thread ("" if none). */
+const char* mla_last_error(void);
+
+/* MLA_ABI_VERSION of the loaded library. */
+int mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MLA_H */

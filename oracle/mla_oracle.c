@@ -159,8 +159,11 @@ int oracle_cache_write(int B, int s, int max_seq_len, int fp8, const uint16_t* k
                        const uint16_t* pe_new, const int32_t* start_pos, void* kv_cache,
                        float* kv_scale, uint16_t* pe_cache) {
   if (B < 0 || s < 0 || max_seq_len <= 0) return 1;
-  for (int b = 0; b < B; ++b) {
-    for (int i = 0; i < s; ++i) {
+  /* rows are independent: one (b, i) per iteration */
+#pragma omp parallel for schedule(static)
+  for (long long bi = 0; bi < (long long)B * s; ++bi) {
+    {
+      const int b = (int)(bi / s), i = (int)(bi % s);
       long long r = (long long)start_pos[b] + i;
       if (r < 0 || r >= max_seq_len) continue; /* dropped */
       const uint16_t* src = kv_new + ((size_t)b * s + i) * ORC_C;

@@ -1,0 +1,227 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars (float outputs are compared in float64 against the oracle's fp64 result):
+  bf16 latent cache:  relative L2 <= 1e-2 and max |err| <= 5e-2
+  FP8 latent cache:   relative L2 <= 3e-2 (and max |err| <= 5e-2)
+  FP8 codes and scales written by mla_cache_write: bit-exact.
+Small cases span several 32-row tiles with ragged tails and are compared in
+full; the five decode workloads at full size run in the launch configuration
+the benchmark uses and are compared on sampled (sequence, head) rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mla_latent_kv_08_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+REL_BF16, ABS_MAX, REL_FP8 = 1e-2, 5e-2, 3e-2
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def m():
+    from mla_latent_kv_08_amd import mla
+    return mla
+
+
+def to_dev(x):
+    return None if x is None else x.to(DEV).contiguous()
+
+
+def errors(out_gpu, ref):
+    g = out_gpu.float().cpu().double().numpy().reshape(ref.shape)
+    assert np.isfinite(g).all(), "non-finite GPU output"
+    rel = np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)
+    return float(rel), float(np.abs(g - ref).max())
+
+
+def check(out_gpu, ref, fp8=False, label=""):
+    rel, mx = errors(out_gpu, ref)
+    print(f"[{label}] relL2={rel:.3e} max|err|={mx:.3e}", flush=True)
+    assert rel <= (REL_FP8 if fp8 else REL_BF16), (label, rel)
+    assert mx <= ABS_MAX, (label, mx)
+
+
+def gpu_caches(m, w, x):
+    """Device caches for inputs x: bf16 rows as given, or FP8 via mla_cache_write."""
+    B, T = w.batch, w.max_seq_len
+    pe = to_dev(x["pe"])
+    if not w.fp8:
+        return to_dev(x["kv"]), None, pe
+    kv8 = torch.zeros(B, T, 512, dtype=torch.uint8, device=DEV)
+    sc = torch.zeros(B, T, 4, dtype=torch.float32, device=DEV)
+    pe_c = torch.zeros(B, T, 64, dtype=torch.bfloat16, device=DEV)
+    m.cache_write(to_dev(x["kv"]), pe, torch.zeros(B, dtype=torch.int32, device=DEV), kv8, pe_c,
+                  kv_scale=sc)
+    return kv8, sc, pe_c
+
+
+def oracle_caches(w, x):
+    if not w.fp8:
+        return x["kv"], None, x["pe"]
+    codes, scales, pe = oracle.cache_write(x["kv"], x["pe"], torch.zeros(w.batch, dtype=torch.int32),
+                                           w.max_seq_len, True)
+    return codes, scales, pe
+
+
+def run_case(m, w, x, pairs=None, label=""):
+    print(f"[{label}] GPU decode B={w.batch} H={w.heads} T={w.max_seq_len} fp8={w.fp8} "
+          f"topk={w.topk}", flush=True)
+    kv, sc, pe = gpu_caches(m, w, x)
+    out = m.decode(to_dev(x["q_nope"]), to_dev(x["q_pe"]), to_dev(x["wkv_b"]), kv, pe,
+                   to_dev(x["cache_lens"]), kv_scale=sc, topk_idx=to_dev(x["topk_idx"]))
+    torch.cuda.synchronize()
+    okv, osc, ope = oracle_caches(w, x)
+    if w.fp8:
+        assert np.array_equal(kv.cpu().numpy(), okv), "FP8 codes differ"
+        assert np.array_equal(sc.cpu().numpy().view(np.uint32), osc.view(np.uint32)), "scales differ"
+    ref = oracle.decode(x["q_nope"], x["q_pe"], x["wkv_b"], okv, ope, x["cache_lens"],
+                        synth.SOFTMAX_SCALE, kv_scale=osc, topk_idx=x["topk_idx"], pairs=pairs)
+    if pairs is not None:
+        got = out.reshape(w.batch, w.heads, 128)[[p[0] for p in pairs], [p[1] for p in pairs]]
+        check(got, ref, w.fp8, label)
+    else:
+        check(out, ref.reshape(w.batch, 1, w.heads, 128), w.fp8, label)
+    return out
+
+
+# ---------------------------------------------------------------- small cases, full compare
+
+@pytest.mark.parametrize("B,H,T", [(1, 16, 256), (2, 128, 300), (3, 48, 97), (1, 100, 33),
+                                   (2, 32, 1), (1, 128, 64)])
+def test_dense_small(m, B, H, T):
+    w = synth.Workload("dense", B, H, T, seed=100 + T)
+    run_case(m, w, synth.make_inputs(w), label=f"dense B{B} H{H} T{T}")
+
+
+def test_ragged_small_with_poison(m):
+    w = synth.Workload("ragged", 6, 64, 1000, ragged=(0, 1000), seed=5)
+    x = synth.make_inputs(w)
+    x["kv"] = x["kv"].clone()
+    x["pe"] = x["pe"].clone()
+    x["cache_lens"] = torch.tensor([0, 1, 31, 33, 1000, 517], dtype=torch.int32)
+    T = w.max_seq_len
+    tail = torch.arange(T).reshape(1, T) >= x["cache_lens"].reshape(-1, 1).long()
+    x["kv"][tail] = float("nan")
+    x["pe"][tail] = float("nan")
+    out = run_case(m, w, x, label="ragged+poison")
+    assert (out[0].float() == 0).all()  # length 0 -> zeros
+
+
+def test_topk_small(m):
+    w = synth.Workload("topk", 3, 128, 2000, topk=300, seed=6)
+    x = synth.make_inputs(w)
+    idx = x["topk_idx"].clone()
+    idx[0, 0, :7] = -1          # padding
+    idx[1, 0, -3:] = 5000       # out of range
+    x["topk_idx"] = idx
+    x["cache_lens"] = torch.tensor([2000, 1500, 2000], dtype=torch.int32)  # b1: entries >= 1500 skipped
+    run_case(m, w, x, label="topk300")
+
+
+def test_topk_all_positions_equals_dense(m):
+    w = synth.Workload("dense", 2, 128, 160, seed=7)
+    x = synth.make_inputs(w)
+    args = [to_dev(x["q_nope"]), to_dev(x["q_pe"]), to_dev(x["wkv_b"]), to_dev(x["kv"]),
+            to_dev(x["pe"]), to_dev(x["cache_lens"])]
+    dense = m.decode(*args)
+    idx = torch.arange(160, dtype=torch.int32).flip(0).reshape(1, 1, 160).expand(2, 1, 160)
+    tk = m.decode(*args, topk_idx=to_dev(idx.contiguous()))
+    rel, mx = errors(tk, dense.float().cpu().double().numpy())
+    assert rel < 1e-2 and mx < 5e-2
+
+
+def test_fp8_small(m):
+    w = synth.Workload("fp8", 2, 128, 200, fp8=True, outlier_frac=0.01, outlier_mult=20.0, seed=8)
+    run_case(m, w, synth.make_inputs(w), label="fp8 small")
+
+
+def test_cache_write_rows_and_dropping(m):
+    for fp8 in (False, True):
+        B, s, T = 4, 5, 12
+        g = torch.Generator().manual_seed(9)
+        kv_new = torch.randn(B, s, 512, generator=g).to(torch.bfloat16)
+        pe_new = torch.randn(B, s, 64, generator=g).to(torch.bfloat16)
+        sp = torch.tensor([0, 9, -2, 3], dtype=torch.int32)
+        kv = torch.zeros(B, T, 512, dtype=torch.uint8 if fp8 else torch.bfloat16, device=DEV)
+        sc = torch.zeros(B, T, 4, dtype=torch.float32, device=DEV) if fp8 else None
+        pe = torch.zeros(B, T, 64, dtype=torch.bfloat16, device=DEV)
+        m.cache_write(to_dev(kv_new), to_dev(pe_new), to_dev(sp), kv, pe, kv_scale=sc)
+        okv, osc, ope = oracle.cache_write(kv_new, pe_new, sp, T, fp8)
+        got_kv = kv.cpu().numpy() if fp8 else kv.cpu().view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got_kv, okv)
+        assert np.array_equal(pe.cpu().view(torch.int16).numpy().view(np.uint16), ope)
+        if fp8:
+            assert np.array_equal(sc.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+
+
+def test_fp8_codec_edge_values(m):
+    # blocks built to hit ties, saturation, signed zeros, subnormal codes and a zero block
+    vals = []
+    for c in range(0x7F):
+        vals.append(oracle.e4m3fn_value(c))
+    v = np.array(vals, np.float32)
+    mids = ((v[1:].astype(np.float64) + v[:-1]) / 2).astype(np.float32)
+    pool = np.concatenate([v, mids, -mids, [0.0, -0.0, 448.0, -448.0, 1e-3, -1e-3]]).astype(np.float32)
+    n_rows = (pool.size + 127) // 128 + 2
+    x = np.zeros(n_rows * 512, np.float32)
+    x[: pool.size] = pool
+    x[-512:-384] = 0.0                       # an all-zero block
+    x[-384:-256] = np.float32(3e-39)         # tiny block (scale underflows)
+    kv_new = torch.from_numpy(x.reshape(1, n_rows, 512)).to(torch.bfloat16)
+    pe_new = torch.zeros(1, n_rows, 64, dtype=torch.bfloat16)
+    kv = torch.zeros(1, n_rows, 512, dtype=torch.uint8, device=DEV)
+    sc = torch.zeros(1, n_rows, 4, dtype=torch.float32, device=DEV)
+    pe = torch.zeros(1, n_rows, 64, dtype=torch.bfloat16, device=DEV)
+    m.cache_write(to_dev(kv_new), to_dev(pe_new), torch.zeros(1, dtype=torch.int32, device=DEV),
+                  kv, pe, kv_scale=sc)
+    okv, osc, _ = oracle.cache_write(kv_new, pe_new, torch.zeros(1, dtype=torch.int32), n_rows, True)
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), osc.view(np.uint32))
+    assert np.array_equal(kv.cpu().numpy(), okv)
+
+
+def test_deterministic_and_no_out_of_bounds_writes(m):
+    w = synth.Workload("det", 3, 128, 700, ragged=(1, 700), seed=10)
+    x = synth.make_inputs(w)
+    args = [to_dev(x["q_nope"]), to_dev(x["q_pe"]), to_dev(x["wkv_b"]), to_dev(x["kv"]),
+            to_dev(x["pe"]), to_dev(x["cache_lens"])]
+    guard = 4096
+    buf = torch.full((2 * guard + 3 * 128 * 128,), -7.0, dtype=torch.bfloat16, device=DEV)
+    out = buf[guard: guard + 3 * 128 * 128].view(3, 1, 128, 128)
+    m.decode(*args, out=out)
+    first = out.clone()
+    m.decode(*args, out=out)
+    assert torch.equal(first.view(torch.int16), out.view(torch.int16))
+    assert (buf[:guard] == -7.0).all() and (buf[-guard:] == -7.0).all()
+
+
+# ---------------------------------------------------------------- the five workloads, full size
+
+def sample_pairs(w, n, seed):
+    rng = np.random.default_rng(seed)
+    b = rng.integers(0, w.batch, n)
+    h = rng.integers(0, w.heads, n)
+    b[:4] = [0, w.batch - 1, 0, w.batch - 1]
+    h[:4] = [0, w.heads - 1, w.heads - 1, 0]
+    return [(int(i), int(j)) for i, j in zip(b, h)]
+
+
+def test_workload_tiny_full(m):
+    w = synth.WORKLOADS["tiny_b1_h16_t256"]
+    run_case(m, w, synth.make_inputs(w), label=w.name)
+
+
+def test_workload_dense_4k_full(m):
+    w = synth.WORKLOADS["dense_b1_h128_t4096"]
+    run_case(m, w, synth.make_inputs(w), label=w.name)
+
+
+@pytest.mark.parametrize("name", ["ragged_b32_h128_t16384", "fp8_b16_h128_t32768",
+                                  "topk2048_b8_h128_t65536"])
+def test_workload_full_sampled(m, name):
+    w = synth.WORKLOADS[name]
+    x = synth.make_inputs(w)
+    run_case(m, w, x, pairs=sample_pairs(w, 64, w.seed), label=name)
