@@ -89,34 +89,42 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
 // ---------------------------------------------------------------------------
 // attention (split-T flash decoding)
 //
-// grid (num_splits, B), 256 threads = 4 waves.  Workgroup (split, b) walks its
-// chunk of the selection in tiles of 32 cache rows held in LDS row-major
-// ([t][576]: 512 latent then 64 rotary values), in a ring of kStages tiles.
-//   scores  S^T = K . Qa^T    A operand: 16-byte row reads of the tile
-//   update  O^T += V^T . P^T  A operand: ds_read_tr16_b64 transposing reads of
-//                             the same tile (V = its first 512 columns)
-// Wave w owns heads 32w..32w+31: Qa for them lives in registers (B operand,
-// 36 k-steps of 16), O^T (512 x 32 fp32) in 16 accumulator blocks.  The S^T
-// accumulator gives every lane one head (l%32) and 16 of the 32 rows (the
-// other 16 sit in lane l^32), so the per-head softmax needs one cross-lane
-// exchange, and the probabilities feed the update as its B operand in place:
-// element e of the S^T block is row 8(e/4) + 4(l/32) + e%4, which is exactly
-// the row order the two transposing reads deliver for k-step e/8.
+// grid (num_splits, B), 256 threads = 4 waves (one per SIMD).  Workgroup
+// (split, b) walks its chunk of the selection in tiles of 32 cache rows held
+// in LDS row-major ([t][576]: 512 latent then 64 rotary values), in a ring of
+// kStages tiles.  Per tile:
+//   1. scores: wave w owns heads 32w..32w+31.  S^T[t][h] = K[t][:] . Qa[h][:]
+//      with 36 MFMA 32x32x16 (A: 16-byte row reads of the tile, B: the wave's
+//      Qa in 144 registers).  Lane l holds head l%32, rows 8(e/4)+4(l/32)+e%4.
+//   2. online softmax of those heads (the other 16 rows of a head sit in lane
+//      l^32); P (bf16) goes to sP[head][tau], tau = row with bits 2 and 3
+//      swapped, which makes each lane's 8 consecutive P values contiguous.
+//   3. update, split by latent columns: wave w owns O^T[c][h] for c in
+//      128w..128w+127 and all 128 heads (16 accumulator blocks, 256 AGPRs).
+//      O^T += V^T . P^T with A = V^T from ds_read_tr16_b64 transposing reads
+//      of the tile (each read feeds 4 head blocks) and B = P^T from sP.
+// Splitting the update by columns keeps the LDS bytes per MFMA low: per tile
+// and workgroup 144 KB of score-operand reads, 32 KB of transposing reads and
+// 40 KB of P traffic.
 //
-// bf16 cache: the tiles are filled by direct global->LDS loads
-// (global_load_lds_dwordx4, no staging registers), kStages-1 tiles ahead.
-// FP8 cache: codes and scales go through registers one tile ahead and are
-// dequantised to bf16(float(code) * scale) when stored.
+// bf16 cache: tiles are filled by direct global->LDS loads, kStages-1 tiles
+// ahead.  FP8 cache: codes and scales go through registers one tile ahead and
+// are dequantised to bf16(float(code) * scale) when stored.
 //
 // LDS swizzle: logical 16-byte chunk ch of row t sits at chunk ch ^ F(t),
-// F(t) = 2(t&3) + ((t>>2)&1).  Eight consecutive rows read the same logical
-// chunk from eight different bank groups, and each 16-lane group of a
-// transposing read touches 16 distinct 8-byte bank slots.
+// F(t) = 4((t>>1)&1) + ((t>>2)&3), which only permutes chunks inside their
+// aligned group of 8.  gfx950 LDS serves 256 bytes per cycle (64 banks): a
+// b128 read is served 16 lanes at a time and a b64 transposing read 32 lanes
+// at a time.  With the 1152-byte row stride this F puts the 16 rows of a score
+// read, and the 4 rows x 4 chunks of a transposing read, on distinct banks.
 // ---------------------------------------------------------------------------
 constexpr int kTT = kTileRows;              // rows per tile
 constexpr int kStages = 4;                  // tiles in the LDS ring
 constexpr int kTileElems = kTT * kQK;       // bf16 elements per tile (36 KB)
 constexpr int kMaxIdx = 1024;               // top-k entries staged in LDS per split
+constexpr int kAttnWaves = 4;
+constexpr int kAttnThreads = 64 * kAttnWaves;
+constexpr int kPStride = 40;                // bf16 per sP row (32 + 8 padding)
 
 struct AttnArgs {
   const uint16_t* qt;
@@ -125,13 +133,13 @@ struct AttnArgs {
   const uint16_t* pe;
   const int32_t* lens;
   const int32_t* topk_idx;
-  float* part_o;
+  uint16_t* part_o;
   float* part_ml;
   int H, Hp, T, topk, NS, CH, head_blocks;
   float scale_log2;
 };
 
-__device__ __forceinline__ int swz(int t) { return ((t & 3) << 1) | ((t >> 2) & 1); }
+__device__ __forceinline__ int swz(int t) { return (((t >> 1) & 1) << 2) | ((t >> 2) & 3); }
 __device__ __forceinline__ int tile_off(int t, int ch) { return t * kQK + ((ch ^ swz(t)) << 3); }
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -158,6 +166,9 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// s_waitcnt vmcnt(n) leaving the other counters unconstrained.
+#define MLA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
+
 // Sequence length clamped to the buffer, and the number of selected entries
 // the splits walk (top-k rows of a sequence with no valid row select nothing).
 __device__ __forceinline__ int seq_len(const int32_t* lens, int b, int T) {
@@ -174,7 +185,7 @@ struct Stage {
 };
 
 template <bool FP8, bool TOPK>
-__global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a) {
   const int split = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -186,13 +197,17 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
   const int ntiles = (p1 - p0 + kTT - 1) / kTT;
 
   // One LDS array per ring slot (not one 2-D array): the slot a tile lives in
-  // is a compile-time constant below, which lets the compiler see that the
-  // LDS-DMA writes in flight target other slots than the one being read, so
-  // it does not wait for them.
+  // is a compile-time constant in the loop body below.
   __shared__ __attribute__((aligned(16))) uint16_t sT0[kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t sT1[kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t sT2[kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t sT3[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t sP[128 * kPStride];
+  __shared__ float sAlpha[128];
+  __shared__ float sL[128];
+  __shared__ uint32_t sMask[kStages];
+  __shared__ uint32_t sRescale[2];  // per tile parity: some head of the tile rescales
+  __shared__ int sIdx[TOPK ? kMaxIdx : 1];
   static_assert(kStages == 4, "one LDS array per ring slot");
   auto slot = [&](auto S) -> uint16_t* {
     constexpr int st = decltype(S)::value;
@@ -201,59 +216,63 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     else if constexpr (st == 2) return sT2;
     else return sT3;
   };
-  __shared__ uint32_t sMask[kStages];
-  __shared__ int sIdx[TOPK ? kMaxIdx : 1];
 
-  const bool active = wave < a.head_blocks;
+  const bool active = wave < a.head_blocks;  // this wave has score heads
   const int n = lane & 31, g = lane >> 5;
   const int head = wave * 32 + n;
   const size_t seq_row0 = (size_t)b * a.T;
 
   if (TOPK) {  // stage this split's row indices; invalid entries become -1
-    for (int i = tid; i < p1 - p0; i += 256) {
+    for (int i = tid; i < p1 - p0; i += kAttnThreads) {
       const int r = a.topk_idx[(size_t)b * a.topk + p0 + i];
       sIdx[i] = (r >= 0 && r < len) ? r : -1;
     }
-    __syncthreads();
   }
+  // P rows of padding heads stay zero
+  for (int i = tid; i < 128 * kPStride / 2; i += kAttnThreads) ((uint32_t*)sP)[i] = 0u;
+  if (tid < 128) sAlpha[tid] = 1.f;
+  if (tid < 2) sRescale[tid] = 0u;
+  __syncthreads();
+
   // Row of tile position t (any valid row when the position selects nothing:
   // its score is masked, and it must only be finite).
-  auto tile_row = [&](int pt, int t, bool& ok) -> int {
+  auto tile_row = [&](int pt, int t) -> int {
     const int pos = pt + t;
     if (TOPK) {
       const int r = pos < p1 ? sIdx[pos - p0] : -1;
-      ok = r >= 0;
-      return ok ? r : 0;
+      return r >= 0 ? r : 0;
     }
-    ok = pos < p1;
-    return ok ? pos : p1 - 1;
+    return pos < p1 ? pos : p1 - 1;
   };
+  // Bit t of a tile's mask: tile row t selects a position.
   auto publish_mask = [&](int pt, int stage) {
-    if (wave == 0) {
-      bool ok = false;
-      if (lane < 32) (void)tile_row(pt, lane, ok);
-      const uint32_t m = (uint32_t)__ballot(ok && lane < 32);
-      if (lane == 0) sMask[stage] = m;
+    if (TOPK) {
+      if (wave == 0) {
+        const int pos = pt + lane;
+        const bool ok = lane < 32 && pos < p1 && sIdx[pos - p0] >= 0;
+        const uint32_t m = (uint32_t)__ballot(ok);
+        if (lane == 0) sMask[stage] = m;
+      }
+    } else if (tid == 0) {
+      const int rows = p1 - pt;
+      sMask[stage] = rows >= 32 ? 0xFFFFFFFFu : ((1u << rows) - 1u);
     }
   };
 
-  // ---- bf16 tiles: direct global -> LDS.  Instruction i of the tile writes LDS
-  // chunks 64i .. 64i+63 (lane order); wave w issues i = w, w+4, ..., w+32.
+  // ---- bf16 tiles: direct global -> LDS.  Instruction i (0..35) of a tile
+  // writes LDS chunks 64i .. 64i+63 in lane order; wave w issues i = w + 4k.
   auto issue_bf16 = [&](int j, auto S) {
     const int pt = p0 + j * kTT, stage = decltype(S)::value;
     uint16_t* dst = slot(S);
-    // Lane position P = 64i + lane walks i = wave, wave+4, ...: P grows by 256
-    // = 3 rows (of 72 chunks) + 40 chunks per instruction.  The position is
-    // laundered so the nine (row, chunk) pairs are recomputed per tile rather
-    // than kept live across the loop.
+    // P = 64i + lane grows by 256 = 3 rows (of 72 chunks) + 40 chunks per
+    // instruction; laundered so it is recomputed per tile, not kept live.
     int P = 64 * wave + lane;
     asm volatile("" : "+v"(P));
     int t = P / 72, phys = P - 72 * t;
 #pragma unroll
     for (int k = 0; k < 9; ++k) {
       const int ch = phys ^ swz(t);
-      bool ok;
-      const size_t row = seq_row0 + tile_row(pt, t, ok);
+      const size_t row = seq_row0 + tile_row(pt, t);
       const uint16_t* src = ch < 64 ? (const uint16_t*)a.kv + row * kC + ch * 8
                                     : a.pe + row * kR + (ch - 64) * 8;
       lds_dma16(src, lds_addr(dst + 512 * (wave + 4 * k)));
@@ -275,14 +294,12 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     const int pt = p0 + j * kTT;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int u = tid + 256 * k, t = u >> 5, cc = u & 31;
-      bool ok;
-      const size_t row = seq_row0 + tile_row(pt, t, ok);
+      const int u = tid + kAttnThreads * k, t = u >> 5, cc = u & 31;
+      const size_t row = seq_row0 + tile_row(pt, t);
       c8[k] = *(const u32x4*)((const uint8_t*)a.kv + row * kC + cc * 16);
       csc[k] = a.kv_scale[row * 4 + (cc >> 3)];
     }
-    bool ok;
-    const size_t row = seq_row0 + tile_row(pt, tid >> 3, ok);
+    const size_t row = seq_row0 + tile_row(pt, tid >> 3);
     pev = *(const u32x4*)(a.pe + row * kR + (tid & 7) * 8);
   };
   auto store_fp8 = [&](int j, auto S) {
@@ -290,7 +307,7 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     uint16_t* dst = slot(S);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int u = tid + 256 * k, t = u >> 5, cc = u & 31;
+      const int u = tid + kAttnThreads * k, t = u >> 5, cc = u & 31;
       uint32_t w[8];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
@@ -305,10 +322,10 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     publish_mask(p0 + j * kTT, stage);
   };
 
-  // O accumulators.  Every definition of o[] is an MFMA result (zero operands
-  // for the initial value and in the rescale below): a VALU definition would
-  // make the compiler keep the loop-carried accumulators in VGPRs and copy
-  // all 256 of them every iteration.
+  // O accumulators o[4 * m + nb]: columns 128w + 32m + ..., heads 32nb + ...
+  // Every definition of o[] is an MFMA result (zero operands for the initial
+  // value and in the rescale below): a VALU definition would make the compiler
+  // keep the loop-carried accumulators in VGPRs and copy them every iteration.
   const u32x4 zq = {0u, 0u, 0u, 0u};
   f32x16 o[16];
 #pragma unroll
@@ -317,24 +334,27 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
 
   // Per-lane LDS bases (element offsets inside a tile).
   //   score k-step st reads logical chunk 2st+g of row n:
-  //     phys = 8(st>>2) + ((2(st&3)+g) ^ F(n))          -> 4 bases + immediates
-  //   update (c-block cb, k-step u, half h): lane 4r+q of 16-lane group G reads
-  //     row 16u + 8h + 4(G>>1) + r, columns 32cb + 16(G&1) + 4q .. +3  -> 2 bases
+  //     phys = 8(st>>2) + ((2(st&3)+g) ^ F(n))                 -> 4 bases
+  //   update (column block m, k-step u, half h): lane 4r+q of 16-lane group
+  //     G reads row 16u + 8h + 4(G>>1) + r, columns
+  //     128w + 32m + 16(G&1) + 4q .. +3                         -> 4 bases
   const int fn = swz(n);
   int sc_base[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) sc_base[k] = n * kQK + (((2 * k + g) ^ fn) << 3);
-  const int G = lane >> 4, i16 = lane & 15, rr = i16 >> 2, qq = i16 & 3;
-  const int tr_t = 4 * (G >> 1) + rr;
+  const int G = lane >> 4, rr = (lane & 15) >> 2, qq = lane & 3;
   const int tr_x = 2 * (G & 1) + (qq >> 1);
-  int tr_base[2];
+  int tr_base[2][2];
 #pragma unroll
-  for (int par = 0; par < 2; ++par)
-    tr_base[par] = tr_t * kQK + (((4 * par + tr_x) ^ swz(tr_t)) << 3) + 4 * (qq & 1);
+  for (int h = 0; h < 2; ++h) {
+    const int tr_t = 8 * h + 4 * (G >> 1) + rr;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      tr_base[h][par] = tr_t * kQK + 128 * wave + (((4 * par + tr_x) ^ swz(tr_t)) << 3) + 4 * (qq & 1);
+  }
 
   // ---- pipeline prologue: the first tiles and the query are loaded together,
-  // and everything is complete before the loop (the loop's own waits then only
-  // concern tiles)
+  // and everything is complete before the loop
   if (FP8) {
     load_fp8(0);
   } else {
@@ -342,15 +362,15 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     if (1 < ntiles) issue_bf16(1, Stage<1>{});
     if (2 < ntiles) issue_bf16(2, Stage<2>{});
   }
-  // Absorbed query + q_pe of this lane's head: k-step s covers elements 16s..16s+15,
-  // lane group g holds 8 of them.
+  // Absorbed query + q_pe of this lane's head: k-step s covers elements
+  // 16s..16s+15, lane group g holds 8 of them.
   u32x4 qreg[36];
   if (active) {
     const u32x4* src = (const u32x4*)(a.qt + ((size_t)b * a.Hp + head) * kQK);
 #pragma unroll
-    for (int s = 0; s < 36; ++s) qreg[s] = src[2 * s + g];
+    for (int st = 0; st < 36; ++st) qreg[st] = src[2 * st + g];
   }
-  __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));  // vmcnt(0)
+  MLA_WAIT_VMCNT(0);
   if (FP8) store_fp8(0, Stage<0>{});
 
   // Tile j lives in ring slot S = j % kStages (a compile-time constant here).
@@ -358,12 +378,13 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     constexpr int st = decltype(S)::value;
     if (!FP8) {
       // tiles j+1 .. j+kStages-2 may stay in flight (9 loads each per thread)
-      if (j + kStages - 2 < ntiles) __builtin_amdgcn_s_waitcnt((9 * (kStages - 2) & 15) | (0x7 << 4) | (0xF << 8) | (((9 * (kStages - 2)) >> 4) << 14));
-      else __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));
+      if (j + kStages - 2 < ntiles) MLA_WAIT_VMCNT(9 * (kStages - 2));
+      else MLA_WAIT_VMCNT(0);
     }
-    // tile j visible to every wave; every wave is done with tile j-1.  The
-    // bf16 path waited on its own LDS-DMA loads above, so a plain s_barrier
-    // suffices (__syncthreads would also wait for the tiles still in flight).
+    // Barrier A: tile j visible to every wave; every wave is done with tile j-1
+    // and with sP.  The bf16 path waited on its own LDS-DMA loads above, so a
+    // plain s_barrier suffices (__syncthreads would also wait for the tiles
+    // still in flight).
     if (FP8) __syncthreads();
     else asm volatile("s_barrier" ::: "memory");
     if (!FP8) {
@@ -371,6 +392,8 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     } else if (j + 1 < ntiles) {
       load_fp8(j + 1);
     }
+    // every wave has passed barrier A, so is done with the previous tile's flag
+    if (tid == 0) sRescale[(st + 1) & 1] = 0u;
     const uint16_t* tile = slot(S);
     if (active) {
       // Scores.  The 36 MFMAs accumulate in VGPRs (inline asm: the compiler
@@ -378,29 +401,30 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
       // Back-to-back MFMAs of one shape accumulating into the same registers
       // need no wait states; the s_nop after the chain covers the MFMA-write ->
       // VALU-read hazard (>= 18 wait states for this 8-pass instruction).
-      // Operand reads run three k-steps ahead of the MFMAs.
+      // Operand reads run four k-steps ahead of the MFMAs.
       f32x16 s;
-      u32x4 ka[4];
+      u32x4 ka[5];
 #pragma unroll
-      for (int st = 0; st < 3; ++st) ka[st] = *(const u32x4*)(tile + sc_base[st & 3] + 64 * (st >> 2));
+      for (int k = 0; k < 4; ++k) ka[k] = *(const u32x4*)(tile + sc_base[k & 3] + 64 * (k >> 2));
 #pragma unroll
-      for (int st = 0; st < 36; ++st) {
-        if (st + 3 < 36)
-          ka[(st + 3) & 3] = *(const u32x4*)(tile + sc_base[(st + 3) & 3] + 64 * ((st + 3) >> 2));
-        if (st == 0)
+      for (int k = 0; k < 36; ++k) {
+        if (k + 4 < 36) ka[(k + 4) % 5] = *(const u32x4*)(tile + sc_base[(k + 4) & 3] + 64 * ((k + 4) >> 2));
+        if (k == 0)
           asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(ka[0]), "v"(qreg[0]));
         else
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(ka[st & 3]), "v"(qreg[st]));
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(ka[k % 5]), "v"(qreg[k]));
       }
       asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s));
       const uint32_t mask = sMask[st];
-      float mx = -INFINITY;
+      if (mask != 0xFFFFFFFFu) {  // partial tile (wave-uniform branch)
+        const uint32_t ml = (mask >> (4 * g)) & 0x0F0F0F0Fu;  // rows 8a + 4g + b -> bit 8a + b
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int t = 8 * (e >> 2) + 4 * g + (e & 3);
-        if (!((mask >> t) & 1u)) s[e] = -INFINITY;
-        mx = fmaxf(mx, s[e]);
+        for (int e = 0; e < 16; ++e)
+          if (!((ml >> (8 * (e >> 2) + (e & 3))) & 1u)) s[e] = -INFINITY;
       }
+      float mx = s[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       // online softmax in log2 units; the running max only moves when the new
       // one exceeds it by more than 8 (probabilities stay <= 2^8), which skips
@@ -409,46 +433,52 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
       const float m_use = (m_run == -INFINITY || mt > m_run + 8.0f) ? fmaxf(mt, m_run) : m_run;
       const float m_sub = (m_use == -INFINITY) ? 0.f : m_use;
       const float alpha = (m_use == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_use);
-      float p[16];
       float lsum = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        p[e] = __builtin_amdgcn_exp2f(fmaf(s[e], a.scale_log2, -m_sub));
-        lsum += p[e];
+        s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], a.scale_log2, -m_sub));
+        lsum += s[e];
       }
       l_run = l_run * alpha + lsum;
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          f32x16 t = o[i];
-          asm volatile("" : "+v"(t));  // scale a copy; o[i] itself stays an MFMA value
-          o[i] = mfma32(zq, zq, t * alpha);
-        }
-      }
       m_run = m_use;
-      const u32x4 pb0 = {pack_bf_finite(p[0], p[1]), pack_bf_finite(p[2], p[3]),
-                         pack_bf_finite(p[4], p[5]), pack_bf_finite(p[6], p[7])};
-      const u32x4 pb1 = {pack_bf_finite(p[8], p[9]), pack_bf_finite(p[10], p[11]),
-                         pack_bf_finite(p[12], p[13]), pack_bf_finite(p[14], p[15])};
-      // Update: each c-block needs four transposing reads (rows 4g+r, 8+4g+r,
-      // 16+4g+r, 24+4g+r); the next block's reads are issued before this
-      // block's MFMAs.
-      u32x2 vt[2][4];
-      {
-        const uint16_t* base = tile + tr_base[0];
+      // P rows 8a + 4g + b land at tau = 16(a>>1) + 8g + 4(a&1) + b: two
+      // contiguous 16-byte pieces per lane
+      uint16_t* prow = sP + head * kPStride + 8 * g;
+      *(u32x4*)(prow) = u32x4{cvt_pk_bf16(s[0], s[1]), cvt_pk_bf16(s[2], s[3]),
+                              cvt_pk_bf16(s[4], s[5]), cvt_pk_bf16(s[6], s[7])};
+      *(u32x4*)(prow + 16) = u32x4{cvt_pk_bf16(s[8], s[9]), cvt_pk_bf16(s[10], s[11]),
+                                   cvt_pk_bf16(s[12], s[13]), cvt_pk_bf16(s[14], s[15])};
+      if (g == 0) sAlpha[head] = alpha;
+      if (alpha != 1.f) sRescale[st & 1] = 1u;  // benign race: every writer stores 1
+    }
+    // Barrier B: all P (and rescale factors) of this tile are in LDS.
+    __syncthreads();
+    if (sRescale[st & 1]) {  // rare: some head's running max moved
+      float al[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) vt[0][q] = ds_read_tr16(base + 8 * q * kQK);
+      for (int nb = 0; nb < 4; ++nb) al[nb] = sAlpha[32 * nb + n];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        f32x16 tcopy = o[i];
+        asm volatile("" : "+v"(tcopy));  // scale a copy; o[i] itself stays an MFMA value
+        o[i] = mfma32(zq, zq, tcopy * al[i & 3]);
       }
+    }
+    // Update: column block m, k-step u: A = 2 transposing reads (rows
+    // 16u + 4g + r and 16u + 8 + 4g + r), B = P^T of head block nb (16 bytes).
 #pragma unroll
-      for (int cb = 0; cb < 16; ++cb) {
-        if (cb + 1 < 16) {
-          const uint16_t* base = tile + tr_base[(cb + 1) & 1] + 64 * ((cb + 1) >> 1);
+    for (int u = 0; u < 2; ++u) {
+      u32x4 pb[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) vt[(cb + 1) & 1][q] = ds_read_tr16(base + 8 * q * kQK);
-        }
-        const u32x2* v = vt[cb & 1];
-        o[cb] = mfma32(u32x4{v[0][0], v[0][1], v[1][0], v[1][1]}, pb0, o[cb]);
-        o[cb] = mfma32(u32x4{v[2][0], v[2][1], v[3][0], v[3][1]}, pb1, o[cb]);
+      for (int nb = 0; nb < 4; ++nb) pb[nb] = *(const u32x4*)(sP + (32 * nb + n) * kPStride + 16 * u + 8 * g);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint16_t* base = tile + 16 * u * kQK + 64 * (m >> 1);
+        const u32x2 v0 = ds_read_tr16(base + tr_base[0][m & 1]);
+        const u32x2 v1 = ds_read_tr16(base + tr_base[1][m & 1]);
+        const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) o[4 * m + nb] = mfma32(va, pb[nb], o[4 * m + nb]);
       }
     }
     if (FP8 && j + 1 < ntiles) store_fp8(j + 1, Stage<(st + 1) % kStages>{});
@@ -460,85 +490,109 @@ __global__ __launch_bounds__(256, 1) void attn_split_kernel(AttnArgs a) {
     if (j0 + 3 < ntiles) body(j0 + 3, Stage<3>{});
   }
 
-  // ---- partial result of this split: O normalised by its own l, plus (m, l)
+  // ---- partial result of this split: O normalised by its own l (bf16), plus
+  // (m, l) in fp32.  Layout [b][h][split][512] keeps each (b, h)'s splits
+  // contiguous for the combine.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (active && head < a.H) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    float* po = a.part_o + (((size_t)b * a.NS + split) * a.H + head) * kC;
+  if (active && g == 0) sL[head] = l_tot;
+  if (active && g == 0 && head < a.H) {
+    float* pm = a.part_ml + (((size_t)b * a.H + head) * a.NS + split) * 2;
+    pm[0] = l_tot > 0.f ? m_run : -INFINITY;
+    pm[1] = l_tot;
+  }
+  __syncthreads();
 #pragma unroll
-    for (int cb = 0; cb < 16; ++cb) {
+  for (int nb = 0; nb < 4; ++nb) {
+    const int h = 32 * nb + n;
+    if (h < a.H) {
+      const float lt = sL[h];
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      uint16_t* po = a.part_o + (((size_t)b * a.H + h) * a.NS + split) * kC + 128 * wave + 4 * g;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = 32 * cb + 8 * q + 4 * g;
-        *(f32x4*)(po + c) = f32x4{o[cb][4 * q] * inv, o[cb][4 * q + 1] * inv,
-                                  o[cb][4 * q + 2] * inv, o[cb][4 * q + 3] * inv};
+      for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x16& ob = o[4 * m + nb];
+          *(u32x2*)(po + 32 * m + 8 * q) =
+              u32x2{pack_bf(ob[4 * q] * inv, ob[4 * q + 1] * inv), pack_bf(ob[4 * q + 2] * inv, ob[4 * q + 3] * inv)};
+        }
       }
-    }
-    if (g == 0) {
-      float* pm = a.part_ml + (((size_t)b * a.NS + split) * a.H + head) * 2;
-      pm[0] = l_tot > 0.f ? m_run : -INFINITY;
-      pm[1] = l_tot;
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// combine: grid (H, B), 64 threads; lane owns 8 consecutive latent columns.
+// combine: grid (H, B, 2 column halves), 256 threads.  Thread (sg = tid/32,
+// co = tid%32) accumulates 8 columns over the splits s = sg, sg+8, ...; the
+// eight split groups are added through LDS.
 //   M = max_s m_s,  w_s = l_s 2^(m_s - M),  o = sum_s w_s O_s / sum_s w_s
-// The split loop is unrolled by 4 so each lane keeps eight 16-byte loads in
-// flight.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ part_o,
-                                                     const float* __restrict__ part_ml,
-                                                     const int32_t* __restrict__ lens,
-                                                     uint16_t* __restrict__ olat, int H, int T,
-                                                     int topk, int NS, int CH) {
-  const int h = blockIdx.x, b = blockIdx.y, lane = threadIdx.x;
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml,
+                                                      const int32_t* __restrict__ lens,
+                                                      uint16_t* __restrict__ olat, int H, int T,
+                                                      int topk, int NS, int CH) {
+  const int h = blockIdx.x, b = blockIdx.y, half = blockIdx.z, tid = threadIdx.x;
+  const int sg = tid >> 5, co = tid & 31;
   const int n_b = selected_entries(seq_len(lens, b, T), topk);
   const int ns = (n_b + CH - 1) / CH;
-  const size_t split_stride = (size_t)H * kC;
-  const float* pm = part_ml + ((size_t)b * NS * H + h) * 2;
-  const float* po = part_o + ((size_t)b * NS * H + h) * kC + 8 * lane;
+  const size_t bh = (size_t)b * H + h;
+  const float* pm = part_ml + bh * NS * 2;
+  const uint16_t* po = part_o + bh * NS * kC + 256 * half + 8 * co;
+  // M: each lane of the wave reads every 64th split's (m, l), then a wave max
   float M = -INFINITY;
-  for (int s = 0; s < ns; ++s) {
-    const float2 ml = *(const float2*)(pm + (size_t)s * H * 2);
+  for (int s = tid & 63; s < ns; s += 64) {
+    const float2 ml = *(const float2*)(pm + 2 * s);
     if (ml.y > 0.f) M = fmaxf(M, ml.x);
   }
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  M = wave_max(M);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  int s = 0;
-  for (; s + 4 <= ns; s += 4) {
-    f32x4 v[4][2];
+  int s = sg;
+  for (; s + 24 < ns; s += 32) {  // four splits of this group in flight
+    u32x4 v[4];
     float w[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float2 ml = *(const float2*)(pm + (size_t)(s + k) * H * 2);
+      const float2 ml = *(const float2*)(pm + 2 * (s + 8 * k));
       w[k] = ml.y > 0.f ? ml.y * exp2f(ml.x - M) : 0.f;
-      v[k][0] = *(const f32x4*)(po + (s + k) * split_stride);
-      v[k][1] = *(const f32x4*)(po + (s + k) * split_stride + 4);
+      v[k] = *(const u32x4*)(po + (size_t)(s + 8 * k) * kC);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      if (w[k] > 0.f) {
-        L += w[k];
-        acc0 += w[k] * v[k][0];
-        acc1 += w[k] * v[k][1];
+      L += w[k];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[2 * j] = fmaf(w[k], bf_lo(v[k][j]), acc[2 * j]);
+        acc[2 * j + 1] = fmaf(w[k], bf_hi(v[k][j]), acc[2 * j + 1]);
       }
     }
   }
-  for (; s < ns; ++s) {
-    const float2 ml = *(const float2*)(pm + (size_t)s * H * 2);
-    if (ml.y > 0.f) {
-      const float w = ml.y * exp2f(ml.x - M);
-      L += w;
-      acc0 += w * *(const f32x4*)(po + s * split_stride);
-      acc1 += w * *(const f32x4*)(po + s * split_stride + 4);
+  for (; s < ns; s += 8) {
+    const float2 ml = *(const float2*)(pm + 2 * s);
+    const float w = ml.y > 0.f ? ml.y * exp2f(ml.x - M) : 0.f;
+    const u32x4 v = *(const u32x4*)(po + (size_t)s * kC);
+    L += w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] = fmaf(w, bf_lo(v[j]), acc[2 * j]);
+      acc[2 * j + 1] = fmaf(w, bf_hi(v[j]), acc[2 * j + 1]);
     }
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint16_t* dst = olat + ((size_t)b * H + h) * kC + 8 * lane;
-  *(u32x4*)dst = u32x4{pack_bf(acc0[0] * inv, acc0[1] * inv), pack_bf(acc0[2] * inv, acc0[3] * inv),
-                       pack_bf(acc1[0] * inv, acc1[1] * inv), pack_bf(acc1[2] * inv, acc1[3] * inv)};
+  __shared__ float red[8][256 + 4];
+  __shared__ float lred[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[sg][8 * co + e] = acc[e];
+  if (co == 0) lred[sg] = L;
+  __syncthreads();
+  float o = 0.f, Lt = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    o += red[k][tid];
+    Lt += lred[k];
+  }
+  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
+  olat[bh * kC + 256 * half + tid] = (uint16_t)f2bf(o * inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -591,7 +645,7 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, hipStream_t s
   const int B = p.batch, H = p.num_heads;
   char* ws = (char*)d.workspace;
   uint16_t* qt = (uint16_t*)(ws + plan.off_qt);
-  float* part_o = (float*)(ws + plan.off_part_o);
+  uint16_t* part_o = (uint16_t*)(ws + plan.off_part_o);
   float* part_ml = (float*)(ws + plan.off_part_ml);
   uint16_t* olat = (uint16_t*)(ws + plan.off_olat);
   hipEvent_t* ev = (hipEvent_t*)p.trace_events;
@@ -629,15 +683,15 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, hipStream_t s
   const dim3 agrid(plan.num_splits, B);
   MLA_TRACE(2);
   const bool fp8 = p.kv_dtype == MLA_KV_FP8_E4M3_B128, topk = p.topk > 0;
-  if (fp8 && topk) attn_split_kernel<true, true><<<agrid, 256, 0, stream>>>(aa);
-  else if (fp8) attn_split_kernel<true, false><<<agrid, 256, 0, stream>>>(aa);
-  else if (topk) attn_split_kernel<false, true><<<agrid, 256, 0, stream>>>(aa);
-  else attn_split_kernel<false, false><<<agrid, 256, 0, stream>>>(aa);
+  if (fp8 && topk) attn_split_kernel<true, true><<<agrid, kAttnThreads, 0, stream>>>(aa);
+  else if (fp8) attn_split_kernel<true, false><<<agrid, kAttnThreads, 0, stream>>>(aa);
+  else if (topk) attn_split_kernel<false, true><<<agrid, kAttnThreads, 0, stream>>>(aa);
+  else attn_split_kernel<false, false><<<agrid, kAttnThreads, 0, stream>>>(aa);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   MLA_TRACE(3);
 
   MLA_TRACE(4);
-  combine_kernel<<<dim3(H, B), 64, 0, stream>>>(part_o, part_ml, d.cache_lens, olat, H,
+  combine_kernel<<<dim3(H, B, 2), 256, 0, stream>>>(part_o, part_ml, d.cache_lens, olat, H,
                                                   p.max_seq_len, p.topk, plan.num_splits,
                                                   plan.chunk_rows);
   if ((err = hipGetLastError()) != hipSuccess) return err;

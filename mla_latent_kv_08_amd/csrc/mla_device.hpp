@@ -40,6 +40,13 @@ __device__ __forceinline__ uint32_t pack_bf(float lo, float hi) {
 __device__ __forceinline__ uint32_t pack_bf_finite(float lo, float hi) {
   return f2bf_finite(lo) | (f2bf_finite(hi) << 16);
 }
+// Two fp32 -> packed bf16 with gfx950's v_cvt_pk_bf16_f32 (round to nearest
+// even); used for values that stay inside the kernel (softmax probabilities).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
 
 // OCP E4M3FN -> fp32 (exact: every E4M3FN value is an fp32 value).
 // Exponent bias 7; exponent field 0 holds subnormals m * 2^-9.

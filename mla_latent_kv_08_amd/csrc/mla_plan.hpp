@@ -43,9 +43,9 @@ inline DecodePlan make_decode_plan(const mla_params& p) {
   size_t off = 0;
   d.off_qt = off;
   off = align256(off + (size_t)B * d.heads_padded * 576 * 2);
-  d.off_part_o = off;
-  off = align256(off + (size_t)B * d.num_splits * H * 512 * 4);
-  d.off_part_ml = off;
+  d.off_part_o = off;  // bf16 [B][H][num_splits][512]
+  off = align256(off + (size_t)B * d.num_splits * H * 512 * 2);
+  d.off_part_ml = off;  // fp32 [B][H][num_splits][2]
   off = align256(off + (size_t)B * d.num_splits * H * 2 * 4);
   d.off_olat = off;
   off = align256(off + (size_t)B * H * 512 * 2);
