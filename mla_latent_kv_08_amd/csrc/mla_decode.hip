@@ -16,8 +16,114 @@
 
 namespace mla {
 
+// Sequence length clamped to the buffer, and the number of entries of the
+// selection (top-k rows of a sequence with no valid row select nothing).
+__device__ __forceinline__ int seq_len(const int32_t* lens, int b, int T) {
+  const int len = lens[b];
+  return len < 0 ? 0 : (len > T ? T : len);
+}
+__device__ __forceinline__ int selected_entries(int len, int topk) {
+  return topk > 0 ? (len > 0 ? topk : 0) : len;
+}
+
+// Inclusive prefix sum over the 256 threads of a workgroup; *total receives
+// the sum of all 256 values.
+__device__ int block_scan_256(int v, int* sc, int* total) {
+  const int tid = threadIdx.x;
+  sc[tid] = v;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int y = tid >= off ? sc[tid - off] : 0;
+    __syncthreads();
+    sc[tid] += y;
+    __syncthreads();
+  }
+  const int r = sc[tid];
+  *total = sc[255];
+  __syncthreads();
+  return r;
+}
+
+// Sum (or max) over the 256 threads of a workgroup, returned to every thread.
+template <bool MAX>
+__device__ long long block_reduce_256(long long v, long long* red) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const long long y = __shfl_xor(v, o, 64);
+    v = MAX ? (y > v ? y : v) : v + y;
+  }
+  if ((tid & 63) == 0) red[tid >> 6] = v;
+  __syncthreads();
+  long long r = red[0];
+#pragma unroll
+  for (int k = 1; k < 4; ++k) r = MAX ? (red[k] > r ? red[k] : r) : r + red[k];
+  __syncthreads();
+  return r;
+}
+
+constexpr int kPlanCache = 4096;  // tile counts kept in LDS by the planner
+
+// Work plan of one decode call, computed by one workgroup of 256 threads (the
+// split is described with make_decode_plan): picks the tile budget S, then
+// writes wcum[b] = k_0 + ... + k_{b-1} (wcum[B] = workgroups in use) and
+// wg_seq[i] = the sequence of workgroup i.
+__device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min_tiles,
+                            int32_t* wcum, int32_t* wg_seq) {
+  __shared__ int tl[kPlanCache];
+  __shared__ int sc[256];
+  __shared__ long long red[4];
+  const int tid = threadIdx.x;
+  auto tiles_of = [&](int bb) -> int {
+    return (selected_entries(seq_len(lens, bb, T), topk) + kTileRows - 1) / kTileRows;
+  };
+  auto tiles = [&](int bb) -> int { return bb < kPlanCache ? tl[bb] : tiles_of(bb); };
+  long long tot = 0, mx = 0;
+  for (int bb = tid; bb < B; bb += 256) {
+    const int t = tiles_of(bb);
+    if (bb < kPlanCache) tl[bb] = t;
+    tot += t;
+    mx = t > mx ? t : mx;
+  }
+  __syncthreads();
+  tot = block_reduce_256<false>(tot, red);
+  mx = block_reduce_256<true>(mx, red);
+  // workgroups needed with budget S
+  auto groups_for = [&](long long S) -> long long {
+    long long c = 0;
+    for (int bb = tid; bb < B; bb += 256) c += (tiles(bb) + S - 1) / S;
+    return block_reduce_256<false>(c, red);
+  };
+  long long S = mx > 0 ? mx : 1;
+  if (mx > 0 && groups_for(mx) <= kTargetCUs) {
+    long long lo = (tot + kTargetCUs - 1) / kTargetCUs, hi = mx;  // groups_for(hi) fits
+    if (lo < 1) lo = 1;
+    while (lo < hi) {  // smallest S in [lo, hi] that fits (groups_for is non-increasing)
+      const long long mid = (lo + hi) / 2;
+      if (groups_for(mid) <= kTargetCUs) hi = mid;
+      else lo = mid + 1;
+    }
+    S = lo;
+  }
+  if (S < min_tiles) S = min_tiles;
+  if (topk > 0 && S > kMaxTopkGroupTiles) S = kMaxTopkGroupTiles;
+  int run = 0, total;
+  for (int base = 0; base < B; base += 256) {
+    const int bb = base + tid;
+    const int k = bb < B ? (int)((tiles(bb) + S - 1) / S) : 0;
+    const int incl = block_scan_256(k, sc, &total);
+    if (bb < B) {
+      wcum[bb + 1] = run + incl;
+      for (int i = run + incl - k; i < run + incl; ++i) wg_seq[i] = bb;
+    }
+    run += total;
+  }
+  if (tid == 0) wcum[0] = 0;
+}
+
 // ---------------------------------------------------------------------------
-// absorb: grid (heads_padded, 4 column blocks of 128), 256 threads.
+// absorb: grid (heads_padded + 1, 4 column blocks of 128), 256 threads.
+// Workgroup (heads_padded, 0) computes the attention work plan instead.
 // Thread (cq = tid%16, dq = tid/16) keeps W_UK[h][8dq..8dq+7][c0..c0+7] in
 // registers and accumulates over its 8 rows of d for every sequence; the 16
 // partial sums per column are added through LDS.  Output row layout of qt:
@@ -27,8 +133,14 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ q_pe,
                                                      const uint16_t* __restrict__ wkv_b,
                                                      uint16_t* __restrict__ qt, int B, int H,
-                                                     int Hp) {
+                                                     int Hp, const int32_t* __restrict__ lens,
+                                                     int T, int topk, int min_group_tiles,
+                                                     int32_t* wcum, int32_t* wg_seq) {
   const int h = blockIdx.x, cblk = blockIdx.y, tid = threadIdx.x;
+  if (h == Hp) {
+    if (cblk == 0) plan_groups(lens, B, T, topk, min_group_tiles, wcum, wg_seq);
+    return;
+  }
   const int cq = tid & 15, dq = tid >> 4;
   const int c0 = cblk * 128 + cq * 8;
   if (h >= H) {  // padding heads: zero rows (the attention waves read them)
@@ -87,11 +199,13 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// attention (split-T flash decoding)
+// attention (split-T flash decoding over a balanced tile split)
 //
-// grid (num_splits, B), 256 threads = 4 waves (one per SIMD).  Workgroup
-// (split, b) walks its chunk of the selection in tiles of 32 cache rows held
-// in LDS row-major ([t][576]: 512 latent then 64 rotary values), in a ring of
+// grid: the workgroups of the plan (one round of at most one per CU in the
+// usual case), 256 threads = 4 waves (one per SIMD).  Workgroup i handles a
+// run of tiles of one sequence (see make_decode_plan) and writes its partial
+// (O / l, m, l) into slot i.  Its tiles (32 cache rows in LDS, row-major
+// [t][576]: 512 latent then 64 rotary values) stream through a ring of
 // kStages tiles.  Per tile:
 //   1. scores: wave w owns heads 32w..32w+31.  S^T[t][h] = K[t][:] . Qa[h][:]
 //      with 36 MFMA 32x32x16 (A: 16-byte row reads of the tile, B: the wave's
@@ -105,11 +219,17 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
 //      of the tile (each read feeds 4 head blocks) and B = P^T from sP.
 // Splitting the update by columns keeps the LDS bytes per MFMA low: per tile
 // and workgroup 144 KB of score-operand reads, 32 KB of transposing reads and
-// 40 KB of P traffic.
+// 40 KB of P traffic.  At the end the normalised O is staged in the idle ring
+// as bf16 rows and written out as whole 1 KB rows per head.
 //
-// bf16 cache: tiles are filled by direct global->LDS loads, kStages-1 tiles
-// ahead.  FP8 cache: codes and scales go through registers one tile ahead and
-// are dequantised to bf16(float(code) * scale) when stored.
+// bf16 cache: tile j+1 is copied global -> LDS directly (no registers) while
+// tile j is processed, its nine loads per thread spread over the score MFMAs.
+// One tile in flight per workgroup keeps the loads from ever waiting for
+// queue space (a second queued tile makes the issuing wave stall until the
+// first lands), and with one workgroup per CU it sustains most of the HBM
+// bandwidth.  FP8 cache: codes and scales of tile j+1 go through registers
+// and are dequantised to bf16(float(code) * scale) when written to LDS after
+// the update.
 //
 // LDS swizzle: logical 16-byte chunk ch of row t sits at chunk ch ^ F(t),
 // F(t) = 4((t>>1)&1) + ((t>>2)&3), which only permutes chunks inside their
@@ -119,12 +239,14 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
 // read, and the 4 rows x 4 chunks of a transposing read, on distinct banks.
 // ---------------------------------------------------------------------------
 constexpr int kTT = kTileRows;              // rows per tile
-constexpr int kStages = 4;                  // tiles in the LDS ring
+constexpr int kStages = 2;                  // tiles in the LDS ring
 constexpr int kTileElems = kTT * kQK;       // bf16 elements per tile (36 KB)
-constexpr int kMaxIdx = 1024;               // top-k entries staged in LDS per split
+constexpr int kMaxIdx = kMaxTopkGroupTiles * kTT;  // top-k entries staged per workgroup
 constexpr int kAttnWaves = 4;
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kPStride = 40;                // bf16 per sP row (32 + 8 padding)
+constexpr int kOStride = 520;               // bf16 per staged output row (512 + 8 padding)
+static_assert(32 * kOStride <= kTileElems, "a 32-head block of O fits one ring slot");
 
 struct AttnArgs {
   const uint16_t* qt;
@@ -133,9 +255,11 @@ struct AttnArgs {
   const uint16_t* pe;
   const int32_t* lens;
   const int32_t* topk_idx;
-  uint16_t* part_o;
-  float* part_ml;
-  int H, Hp, T, topk, NS, CH, head_blocks;
+  const int32_t* wcum;    // [B + 1] first workgroup of each sequence
+  const int32_t* wg_seq;  // [grid] sequence of each workgroup
+  uint16_t* part_o;       // [grid][H][512]
+  float* part_ml;         // [grid][H][2]
+  int B, H, Hp, T, topk, head_blocks;
   float scale_log2;
 };
 
@@ -152,13 +276,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // 16-byte global -> LDS copy for each lane: lane l's 16 bytes from `src` land
-// at LDS byte address base + 16 l (base must be wave-uniform).  Written as
+// at LDS byte address base + OFF + 16 l (base must be wave-uniform).  Written as
 // inline asm so the compiler's wait-count tracking does not treat every later
 // LDS read as possibly depending on it; completion is awaited explicitly with
 // s_waitcnt vmcnt before the workgroup barrier that publishes the tile.
+template <int OFF>
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base)
-               : "memory", "m0");
+  asm volatile("s_add_u32 m0, %1, %2\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base), "i"(OFF)
+               : "memory", "m0", "scc");
 }
 
 __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
@@ -168,16 +293,13 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
 
 // s_waitcnt vmcnt(n) leaving the other counters unconstrained.
 #define MLA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
-
-// Sequence length clamped to the buffer, and the number of selected entries
-// the splits walk (top-k rows of a sequence with no valid row select nothing).
-__device__ __forceinline__ int seq_len(const int32_t* lens, int b, int T) {
-  const int len = lens[b];
-  return len < 0 ? 0 : (len > T ? T : len);
-}
-__device__ __forceinline__ int selected_entries(int len, int topk) {
-  return topk > 0 ? (len > 0 ? topk : 0) : len;
-}
+// Workgroup barrier that publishes this wave's LDS writes but, unlike
+// __syncthreads, does not wait for its global loads still in flight.
+#define MLA_LDS_BARRIER()                                           \
+  do {                                                              \
+    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0) only */      \
+    asm volatile("s_barrier" ::: "memory");                         \
+  } while (0)
 
 template <int S>
 struct Stage {
@@ -185,57 +307,82 @@ struct Stage {
 };
 
 template <bool FP8, bool TOPK>
-__global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a) {
-  const int split = blockIdx.x, b = blockIdx.y;
+__global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
+  const int grp = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int len = seq_len(a.lens, b, a.T);
-  const int n_b = selected_entries(len, TOPK ? a.topk : 0);
-  const int p0 = split * a.CH;
-  if (p0 >= n_b) return;  // whole workgroup: nothing selected in this split
-  const int p1 = min(p0 + a.CH, n_b);
-  const int ntiles = (p1 - p0 + kTT - 1) / kTT;
+  if (grp >= a.wcum[a.B]) return;  // whole workgroup: not used by the plan
+  const int b = a.wg_seq[grp];
+  const int wb = a.wcum[b], kb = a.wcum[b + 1] - wb, piece = grp - wb;
+  const int len = a.lens[b] < 0 ? 0 : (a.lens[b] > a.T ? a.T : a.lens[b]);
+  const int n_b = TOPK ? (len > 0 ? a.topk : 0) : len;
+  const int tb = (n_b + kTT - 1) / kTT;
+  const int t_lo = (int)((long long)piece * tb / kb), t_hi = (int)((long long)(piece + 1) * tb / kb);
+  const int p0 = t_lo * kTT, p1 = min(t_hi * kTT, n_b);
+  const int ntiles = t_hi - t_lo;
+  const size_t seq_row0 = (size_t)b * a.T;
+  const size_t slot_id = grp;
 
   // One LDS array per ring slot (not one 2-D array): the slot a tile lives in
   // is a compile-time constant in the loop body below.
   __shared__ __attribute__((aligned(16))) uint16_t sT0[kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t sT1[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t sT2[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t sT3[kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t sP[128 * kPStride];
   __shared__ float sAlpha[128];
   __shared__ float sL[128];
   __shared__ uint32_t sMask[kStages];
   __shared__ uint32_t sRescale[2];  // per tile parity: some head of the tile rescales
   __shared__ int sIdx[TOPK ? kMaxIdx : 1];
-  static_assert(kStages == 4, "one LDS array per ring slot");
+  static_assert(kStages == 2, "one LDS array per ring slot");
   auto slot = [&](auto S) -> uint16_t* {
     constexpr int st = decltype(S)::value;
     if constexpr (st == 0) return sT0;
-    else if constexpr (st == 1) return sT1;
-    else if constexpr (st == 2) return sT2;
-    else return sT3;
+    else return sT1;
   };
 
   const bool active = wave < a.head_blocks;  // this wave has score heads
   const int n = lane & 31, g = lane >> 5;
   const int head = wave * 32 + n;
-  const size_t seq_row0 = (size_t)b * a.T;
 
-  if (TOPK) {  // stage this split's row indices; invalid entries become -1
+  // P rows and l of heads without a score wave stay zero; their alpha stays 1
+  for (int i = tid; i < 128 * kPStride / 2; i += kAttnThreads) ((uint32_t*)sP)[i] = 0u;
+  if (tid < 128) {
+    sAlpha[tid] = 1.f;
+    sL[tid] = 0.f;
+  }
+
+  // Per-lane LDS bases (element offsets inside a tile).
+  //   score k-step st reads logical chunk 2st+g of row n:
+  //     phys = 8(st>>2) + ((2(st&3)+g) ^ F(n))                 -> 4 bases
+  //   update (column block m, k-step u, half h): lane 4r+q of 16-lane group
+  //     Q reads row 16u + 8h + 4(Q>>1) + r, columns
+  //     128w + 32m + 16(Q&1) + 4q .. +3                         -> 4 bases
+  const int fn = swz(n);
+  int sc_base[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) sc_base[k] = n * kQK + (((2 * k + g) ^ fn) << 3);
+  const int lq = lane >> 4, rr = (lane & 15) >> 2, qq = lane & 3;
+  const int tr_x = 2 * (lq & 1) + (qq >> 1);
+  int tr_base[2][2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int tr_t = 8 * h + 4 * (lq >> 1) + rr;
+#pragma unroll
+    for (int par = 0; par < 2; ++par)
+      tr_base[h][par] = tr_t * kQK + 128 * wave + (((4 * par + tr_x) ^ swz(tr_t)) << 3) + 4 * (qq & 1);
+  }
+
+  if (TOPK) {  // stage this workgroup's row indices; invalid entries become -1
     for (int i = tid; i < p1 - p0; i += kAttnThreads) {
       const int r = a.topk_idx[(size_t)b * a.topk + p0 + i];
       sIdx[i] = (r >= 0 && r < len) ? r : -1;
     }
   }
-  // P rows of padding heads stay zero
-  for (int i = tid; i < 128 * kPStride / 2; i += kAttnThreads) ((uint32_t*)sP)[i] = 0u;
-  if (tid < 128) sAlpha[tid] = 1.f;
   if (tid < 2) sRescale[tid] = 0u;
   __syncthreads();
 
-  // Row of tile position t (any valid row when the position selects nothing:
-  // its score is masked, and it must only be finite).
+  // Row of tile position t (any valid row when the position selects
+  // nothing: its score is masked, and it must only be finite).
   auto tile_row = [&](int pt, int t) -> int {
     const int pos = pt + t;
     if (TOPK) {
@@ -261,29 +408,55 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
 
   // ---- bf16 tiles: direct global -> LDS.  Instruction i (0..35) of a tile
   // writes LDS chunks 64i .. 64i+63 in lane order; wave w issues i = w + 4k.
-  auto issue_bf16 = [&](int j, auto S) {
-    const int pt = p0 + j * kTT, stage = decltype(S)::value;
-    uint16_t* dst = slot(S);
-    // P = 64i + lane grows by 256 = 3 rows (of 72 chunks) + 40 chunks per
-    // instruction; laundered so it is recomputed per tile, not kept live.
+  // Lane position P = 64i + lane grows by 256 = 3 rows (of 72 chunks) + 40
+  // chunks per instruction.
+  struct DmaCursor {
+    int t, phys;
+  };
+  auto dma_start = [&]() -> DmaCursor {
     int P = 64 * wave + lane;
-    asm volatile("" : "+v"(P));
-    int t = P / 72, phys = P - 72 * t;
-#pragma unroll
-    for (int k = 0; k < 9; ++k) {
-      const int ch = phys ^ swz(t);
-      const size_t row = seq_row0 + tile_row(pt, t);
-      const uint16_t* src = ch < 64 ? (const uint16_t*)a.kv + row * kC + ch * 8
-                                    : a.pe + row * kR + (ch - 64) * 8;
-      lds_dma16(src, lds_addr(dst + 512 * (wave + 4 * k)));
-      phys += 40;
-      t += 3;
-      if (phys >= 72) {
-        phys -= 72;
-        t += 1;
-      }
+    asm volatile("" : "+v"(P));  // recomputed per tile, not kept live
+    const int t = P / 72;
+    return DmaCursor{t, P - 72 * t};
+  };
+  // base: LDS byte address of the tile slot plus 1024 * wave, laundered so
+  // the compiler keeps one value per tile instead of nine per slot.
+  auto dma_base = [&](uint16_t* dst) -> uint32_t {
+    uint32_t base = lds_addr(dst) + 1024u * wave;
+    asm volatile("" : "+s"(base));
+    return base;
+  };
+  auto dma_step = [&](DmaCursor& c, int pt, uint32_t base, auto K) {
+    constexpr int k = decltype(K)::value;
+    const int ch = c.phys ^ swz(c.t);
+    const size_t row = seq_row0 + tile_row(pt, c.t);
+    const uint16_t* src = ch < 64 ? (const uint16_t*)a.kv + row * kC + ch * 8
+                                  : a.pe + row * kR + (ch - 64) * 8;
+    lds_dma16<4096 * k>(src, base);
+    c.phys += 40;
+    c.t += 3;
+    if (c.phys >= 72) {
+      c.phys -= 72;
+      c.t += 1;
     }
-    publish_mask(pt, stage);
+  };
+  auto dma_all = [&](DmaCursor& c, int pt, uint32_t base) {
+    dma_step(c, pt, base, Stage<0>{});
+    dma_step(c, pt, base, Stage<1>{});
+    dma_step(c, pt, base, Stage<2>{});
+    dma_step(c, pt, base, Stage<3>{});
+    dma_step(c, pt, base, Stage<4>{});
+    dma_step(c, pt, base, Stage<5>{});
+    dma_step(c, pt, base, Stage<6>{});
+    dma_step(c, pt, base, Stage<7>{});
+    dma_step(c, pt, base, Stage<8>{});
+  };
+  auto issue_bf16 = [&](int j, auto S) {
+    const int pt = p0 + j * kTT;
+    DmaCursor c = dma_start();
+    const uint32_t base = dma_base(slot(S));
+    dma_all(c, pt, base);
+    publish_mask(pt, decltype(S)::value);
   };
 
   // ---- FP8 tiles through registers: 4 units of 16 codes + 1 rotary chunk per thread
@@ -324,44 +497,19 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
 
   // O accumulators o[4 * m + nb]: columns 128w + 32m + ..., heads 32nb + ...
   // Every definition of o[] is an MFMA result (zero operands for the initial
-  // value and in the rescale below): a VALU definition would make the compiler
-  // keep the loop-carried accumulators in VGPRs and copy them every iteration.
+  // value and in the rescale below): a VALU definition would make the
+  // compiler keep the loop-carried accumulators in VGPRs and copy them every
+  // iteration.
   const u32x4 zq = {0u, 0u, 0u, 0u};
   f32x16 o[16];
 #pragma unroll
   for (int i = 0; i < 16; ++i) o[i] = mfma32(zq, zq, f32x16{});
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Per-lane LDS bases (element offsets inside a tile).
-  //   score k-step st reads logical chunk 2st+g of row n:
-  //     phys = 8(st>>2) + ((2(st&3)+g) ^ F(n))                 -> 4 bases
-  //   update (column block m, k-step u, half h): lane 4r+q of 16-lane group
-  //     G reads row 16u + 8h + 4(G>>1) + r, columns
-  //     128w + 32m + 16(G&1) + 4q .. +3                         -> 4 bases
-  const int fn = swz(n);
-  int sc_base[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) sc_base[k] = n * kQK + (((2 * k + g) ^ fn) << 3);
-  const int G = lane >> 4, rr = (lane & 15) >> 2, qq = lane & 3;
-  const int tr_x = 2 * (G & 1) + (qq >> 1);
-  int tr_base[2][2];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int tr_t = 8 * h + 4 * (G >> 1) + rr;
-#pragma unroll
-    for (int par = 0; par < 2; ++par)
-      tr_base[h][par] = tr_t * kQK + 128 * wave + (((4 * par + tr_x) ^ swz(tr_t)) << 3) + 4 * (qq & 1);
-  }
-
-  // ---- pipeline prologue: the first tiles and the query are loaded together,
-  // and everything is complete before the loop
-  if (FP8) {
-    load_fp8(0);
-  } else {
-    issue_bf16(0, Stage<0>{});
-    if (1 < ntiles) issue_bf16(1, Stage<1>{});
-    if (2 < ntiles) issue_bf16(2, Stage<2>{});
-  }
+  // ---- pipeline prologue: the first tiles and the query are loaded
+  // together, and everything is complete before the loop
+  if (!FP8) issue_bf16(0, Stage<0>{});
+  else load_fp8(0);
   // Absorbed query + q_pe of this lane's head: k-step s covers elements
   // 16s..16s+15, lane group g holds 8 of them.
   u32x4 qreg[36];
@@ -376,44 +524,55 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
   // Tile j lives in ring slot S = j % kStages (a compile-time constant here).
   auto body = [&](int j, auto S) {
     constexpr int st = decltype(S)::value;
-    if (!FP8) {
-      // tiles j+1 .. j+kStages-2 may stay in flight (9 loads each per thread)
-      if (j + kStages - 2 < ntiles) MLA_WAIT_VMCNT(9 * (kStages - 2));
-      else MLA_WAIT_VMCNT(0);
-    }
-    // Barrier A: tile j visible to every wave; every wave is done with tile j-1
-    // and with sP.  The bf16 path waited on its own LDS-DMA loads above, so a
-    // plain s_barrier suffices (__syncthreads would also wait for the tiles
-    // still in flight).
-    if (FP8) __syncthreads();
-    else asm volatile("s_barrier" ::: "memory");
-    if (!FP8) {
-      if (j + kStages - 1 < ntiles) issue_bf16(j + kStages - 1, Stage<(st + kStages - 1) % kStages>{});
-    } else if (j + 1 < ntiles) {
-      load_fp8(j + 1);
-    }
+    constexpr int s1 = (st + 1) % kStages;  // slot of tile j + 1 (held tile j - 1)
+    // Barrier A: tile j visible to every wave (the bf16 path first waits for
+    // its own loads of it); every wave is done with tile j-1 and with sP.
+    if (!FP8) MLA_WAIT_VMCNT(0);
+    MLA_LDS_BARRIER();
+    const bool issue = !FP8 && j + 1 < ntiles;
+    const int pt_next = p0 + (j + 1) * kTT;
+    DmaCursor cur = dma_start();
+    const uint32_t nbase = dma_base(slot(Stage<s1>{}));
+    if (issue) publish_mask(pt_next, s1);
+    if (FP8 && j + 1 < ntiles) load_fp8(j + 1);
     // every wave has passed barrier A, so is done with the previous tile's flag
-    if (tid == 0) sRescale[(st + 1) & 1] = 0u;
+    if (tid == 0) sRescale[(j + 1) & 1] = 0u;
     const uint16_t* tile = slot(S);
     if (active) {
       // Scores.  The 36 MFMAs accumulate in VGPRs (inline asm: the compiler
       // would put this accumulator in AGPRs, where O already takes all 256).
       // Back-to-back MFMAs of one shape accumulating into the same registers
-      // need no wait states; the s_nop after the chain covers the MFMA-write ->
-      // VALU-read hazard (>= 18 wait states for this 8-pass instruction).
+      // need no wait states; the s_nop after the chain covers the MFMA-write
+      // -> VALU-read hazard (>= 18 wait states for this 8-pass instruction).
       // Operand reads run four k-steps ahead of the MFMAs.
       f32x16 s;
       u32x4 ka[5];
 #pragma unroll
       for (int k = 0; k < 4; ++k) ka[k] = *(const u32x4*)(tile + sc_base[k & 3] + 64 * (k >> 2));
+      // nine explicitly instantiated groups of four k-steps, one load of tile
+      // j+1 in each (keeps the chain fully unrolled with the loads inside)
+      auto group = [&](auto Q) {
+        constexpr int q = decltype(Q)::value;
 #pragma unroll
-      for (int k = 0; k < 36; ++k) {
-        if (k + 4 < 36) ka[(k + 4) % 5] = *(const u32x4*)(tile + sc_base[(k + 4) & 3] + 64 * ((k + 4) >> 2));
-        if (k == 0)
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(ka[0]), "v"(qreg[0]));
-        else
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(ka[k % 5]), "v"(qreg[k]));
-      }
+        for (int kk = 0; kk < 4; ++kk) {
+          const int k = 4 * q + kk;
+          if (k + 4 < 36) ka[(k + 4) % 5] = *(const u32x4*)(tile + sc_base[(k + 4) & 3] + 64 * ((k + 4) >> 2));
+          if (k == 0)
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(ka[0]), "v"(qreg[0]));
+          else
+            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(ka[k % 5]), "v"(qreg[k]));
+          if (kk == 1 && issue) dma_step(cur, pt_next, nbase, Q);
+        }
+      };
+      group(Stage<0>{});
+      group(Stage<1>{});
+      group(Stage<2>{});
+      group(Stage<3>{});
+      group(Stage<4>{});
+      group(Stage<5>{});
+      group(Stage<6>{});
+      group(Stage<7>{});
+      group(Stage<8>{});
       asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s));
       const uint32_t mask = sMask[st];
       if (mask != 0xFFFFFFFFu) {  // partial tile (wave-uniform branch)
@@ -426,9 +585,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
 #pragma unroll
       for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // online softmax in log2 units; the running max only moves when the new
-      // one exceeds it by more than 8 (probabilities stay <= 2^8), which skips
-      // most rescales of O without changing the result
+      // online softmax in log2 units; the running max only moves when the
+      // new one exceeds it by more than 8 (probabilities stay <= 2^8), which
+      // skips most rescales of O without changing the result
       const float mt = mx * a.scale_log2;
       const float m_use = (m_run == -INFINITY || mt > m_run + 8.0f) ? fmaxf(mt, m_run) : m_run;
       const float m_sub = (m_use == -INFINITY) ? 0.f : m_use;
@@ -449,11 +608,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
       *(u32x4*)(prow + 16) = u32x4{cvt_pk_bf16(s[8], s[9]), cvt_pk_bf16(s[10], s[11]),
                                    cvt_pk_bf16(s[12], s[13]), cvt_pk_bf16(s[14], s[15])};
       if (g == 0) sAlpha[head] = alpha;
-      if (alpha != 1.f) sRescale[st & 1] = 1u;  // benign race: every writer stores 1
+      if (alpha != 1.f) sRescale[j & 1] = 1u;  // benign race: every writer stores 1
+    } else if (issue) {
+      dma_all(cur, pt_next, nbase);
     }
     // Barrier B: all P (and rescale factors) of this tile are in LDS.
-    __syncthreads();
-    if (sRescale[st & 1]) {  // rare: some head's running max moved
+    MLA_LDS_BARRIER();
+    if (sRescale[j & 1]) {  // rare: some head's running max moved
       float al[4];
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb) al[nb] = sAlpha[32 * nb + n];
@@ -481,82 +642,102 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_split_kernel(AttnArgs a)
         for (int nb = 0; nb < 4; ++nb) o[4 * m + nb] = mfma32(va, pb[nb], o[4 * m + nb]);
       }
     }
-    if (FP8 && j + 1 < ntiles) store_fp8(j + 1, Stage<(st + 1) % kStages>{});
+    if (FP8 && j + 1 < ntiles) store_fp8(j + 1, Stage<s1>{});
   };
   for (int j0 = 0; j0 < ntiles; j0 += kStages) {
     body(j0, Stage<0>{});
     if (j0 + 1 < ntiles) body(j0 + 1, Stage<1>{});
-    if (j0 + 2 < ntiles) body(j0 + 2, Stage<2>{});
-    if (j0 + 3 < ntiles) body(j0 + 3, Stage<3>{});
   }
 
-  // ---- partial result of this split: O normalised by its own l (bf16), plus
-  // (m, l) in fp32.  Layout [b][h][split][512] keeps each (b, h)'s splits
-  // contiguous for the combine.
+  // ---- partial result: (m, l) in fp32 and O / l in bf16,
+  // staged through the idle ring (head blocks 0-1, then 2-3, in slots 0-1;
+  // rows of kOStride) so that every head's 512 values leave as one 1 KB row.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (active && g == 0) sL[head] = l_tot;
-  if (active && g == 0 && head < a.H) {
-    float* pm = a.part_ml + (((size_t)b * a.H + head) * a.NS + split) * 2;
-    pm[0] = l_tot > 0.f ? m_run : -INFINITY;
-    pm[1] = l_tot;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int h = 32 * nb + n;
-    if (h < a.H) {
-      const float lt = sL[h];
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      uint16_t* po = a.part_o + (((size_t)b * a.H + h) * a.NS + split) * kC + 128 * wave + 4 * g;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x16& ob = o[4 * m + nb];
-          *(u32x2*)(po + 32 * m + 8 * q) =
-              u32x2{pack_bf(ob[4 * q] * inv, ob[4 * q + 1] * inv), pack_bf(ob[4 * q + 2] * inv, ob[4 * q + 3] * inv)};
-        }
-      }
+  if (active && g == 0) {
+    sL[head] = l_tot;
+    if (head < a.H) {
+      float* pm = a.part_ml + (slot_id * a.H + head) * 2;
+      pm[0] = l_tot > 0.f ? m_run : -INFINITY;
+      pm[1] = l_tot;
     }
+  }
+  __syncthreads();  // ring idle, sL complete
+  auto stage_out = [&](auto NB, auto SL) {
+    constexpr int nb = decltype(NB)::value;
+    const float lt = sL[32 * nb + n];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    uint16_t* row = slot(SL) + n * kOStride + 128 * wave + 4 * g;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f32x16& ob = o[4 * m + nb];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(u32x2*)(row + 32 * m + 8 * q) =
+            u32x2{pack_bf(ob[4 * q] * inv, ob[4 * q + 1] * inv), pack_bf(ob[4 * q + 2] * inv, ob[4 * q + 3] * inv)};
+    }
+  };
+  stage_out(Stage<0>{}, Stage<0>{});
+  stage_out(Stage<1>{}, Stage<1>{});
+  __syncthreads();
+  uint16_t* dst = a.part_o + slot_id * a.H * kC;
+  auto copy_out = [&](auto NB, auto SL) {
+    constexpr int nb = decltype(NB)::value;
+    const uint16_t* srcb = slot(SL);
+#pragma unroll 2
+    for (int i = tid; i < 32 * 64; i += kAttnThreads) {
+      const int h = 32 * nb + (i >> 6), c16 = i & 63;
+      if (h < a.H) *(u32x4*)(dst + (size_t)h * kC + 8 * c16) = *(const u32x4*)(srcb + (i >> 6) * kOStride + 8 * c16);
+    }
+  };
+  copy_out(Stage<0>{}, Stage<0>{});
+  copy_out(Stage<1>{}, Stage<1>{});
+  if (a.H > 64) {  // head blocks 2 and 3 (uniform branch)
+    __syncthreads();
+    stage_out(Stage<2>{}, Stage<0>{});
+    stage_out(Stage<3>{}, Stage<1>{});
+    __syncthreads();
+    copy_out(Stage<2>{}, Stage<0>{});
+    copy_out(Stage<3>{}, Stage<1>{});
   }
 }
 
 // ---------------------------------------------------------------------------
-// combine: grid (H, B, 2 column halves), 256 threads.  Thread (sg = tid/32,
-// co = tid%32) accumulates 8 columns over the splits s = sg, sg+8, ...; the
-// eight split groups are added through LDS.
+// combine: grid (H, B, 2 column halves), 256 threads.  Sequence b's partials
+// sit in slots wcum[b] .. wcum[b+1]-1, one per attention workgroup of b.
+// Thread (sg = tid/32, co = tid%32) accumulates 8 columns over the partials
+// s = sg, sg+8, ...; the eight groups are added through LDS.
 //   M = max_s m_s,  w_s = l_s 2^(m_s - M),  o = sum_s w_s O_s / sum_s w_s
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ part_o,
                                                       const float* __restrict__ part_ml,
-                                                      const int32_t* __restrict__ lens,
-                                                      uint16_t* __restrict__ olat, int H, int T,
-                                                      int topk, int NS, int CH) {
+                                                      const int32_t* __restrict__ wcum,
+                                                      uint16_t* __restrict__ olat, int H) {
   const int h = blockIdx.x, b = blockIdx.y, half = blockIdx.z, tid = threadIdx.x;
   const int sg = tid >> 5, co = tid & 31;
-  const int n_b = selected_entries(seq_len(lens, b, T), topk);
-  const int ns = (n_b + CH - 1) / CH;
+  const size_t s0 = (size_t)wcum[b];
+  const int ns = wcum[b + 1] - wcum[b];
   const size_t bh = (size_t)b * H + h;
-  const float* pm = part_ml + bh * NS * 2;
-  const uint16_t* po = part_o + bh * NS * kC + 256 * half + 8 * co;
-  // M: each lane of the wave reads every 64th split's (m, l), then a wave max
+  const float* pm = part_ml + (s0 * H + h) * 2;
+  const uint16_t* po = part_o + (s0 * H + h) * kC + 256 * half + 8 * co;
+  const size_t ml_stride = (size_t)H * 2, o_stride = (size_t)H * kC;
+  // M: each lane of the wave reads every 64th partial's (m, l), then a wave max
   float M = -INFINITY;
   for (int s = tid & 63; s < ns; s += 64) {
-    const float2 ml = *(const float2*)(pm + 2 * s);
+    const float2 ml = *(const float2*)(pm + s * ml_stride);
     if (ml.y > 0.f) M = fmaxf(M, ml.x);
   }
   M = wave_max(M);
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   int s = sg;
-  for (; s + 24 < ns; s += 32) {  // four splits of this group in flight
+  for (; s + 24 < ns; s += 32) {  // four partials of this group in flight
     u32x4 v[4];
     float w[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const float2 ml = *(const float2*)(pm + 2 * (s + 8 * k));
+      const float2 ml = *(const float2*)(pm + (s + 8 * k) * ml_stride);
       w[k] = ml.y > 0.f ? ml.y * exp2f(ml.x - M) : 0.f;
-      v[k] = *(const u32x4*)(po + (size_t)(s + 8 * k) * kC);
+      v[k] = *(const u32x4*)(po + (size_t)(s + 8 * k) * o_stride);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -569,9 +750,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     }
   }
   for (; s < ns; s += 8) {
-    const float2 ml = *(const float2*)(pm + 2 * s);
+    const float2 ml = *(const float2*)(pm + s * ml_stride);
     const float w = ml.y > 0.f ? ml.y * exp2f(ml.x - M) : 0.f;
-    const u32x4 v = *(const u32x4*)(po + (size_t)s * kC);
+    const u32x4 v = *(const u32x4*)(po + (size_t)s * o_stride);
     L += w;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -656,10 +837,13 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, hipStream_t s
     if (err != hipSuccess) return err;                     \
   }
 
+  int32_t* wcum = (int32_t*)(ws + plan.off_wcum);
+  int32_t* wg_seq = (int32_t*)(ws + plan.off_wg_seq);
+
   MLA_TRACE(0);
-  absorb_kernel<<<dim3(plan.heads_padded, 4), 256, 0, stream>>>(
+  absorb_kernel<<<dim3(plan.heads_padded + 1, 4), 256, 0, stream>>>(
       (const uint16_t*)d.q_nope, (const uint16_t*)d.q_pe, (const uint16_t*)d.wkv_b, qt, B, H,
-      plan.heads_padded);
+      plan.heads_padded, d.cache_lens, p.max_seq_len, p.topk, plan.min_group_tiles, wcum, wg_seq);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   MLA_TRACE(1);
 
@@ -670,30 +854,29 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, hipStream_t s
   aa.pe = (const uint16_t*)d.pe_cache;
   aa.lens = d.cache_lens;
   aa.topk_idx = d.topk_idx;
+  aa.wcum = wcum;
+  aa.wg_seq = wg_seq;
   aa.part_o = part_o;
   aa.part_ml = part_ml;
+  aa.B = B;
   aa.H = H;
   aa.Hp = plan.heads_padded;
   aa.T = p.max_seq_len;
   aa.topk = p.topk;
-  aa.NS = plan.num_splits;
-  aa.CH = plan.chunk_rows;
   aa.head_blocks = plan.head_blocks;
   aa.scale_log2 = p.softmax_scale * 1.4426950408889634f;
-  const dim3 agrid(plan.num_splits, B);
+  const dim3 agrid((unsigned)plan.max_groups);
   MLA_TRACE(2);
   const bool fp8 = p.kv_dtype == MLA_KV_FP8_E4M3_B128, topk = p.topk > 0;
-  if (fp8 && topk) attn_split_kernel<true, true><<<agrid, kAttnThreads, 0, stream>>>(aa);
-  else if (fp8) attn_split_kernel<true, false><<<agrid, kAttnThreads, 0, stream>>>(aa);
-  else if (topk) attn_split_kernel<false, true><<<agrid, kAttnThreads, 0, stream>>>(aa);
-  else attn_split_kernel<false, false><<<agrid, kAttnThreads, 0, stream>>>(aa);
+  if (fp8 && topk) attn_kernel<true, true><<<agrid, kAttnThreads, 0, stream>>>(aa);
+  else if (fp8) attn_kernel<true, false><<<agrid, kAttnThreads, 0, stream>>>(aa);
+  else if (topk) attn_kernel<false, true><<<agrid, kAttnThreads, 0, stream>>>(aa);
+  else attn_kernel<false, false><<<agrid, kAttnThreads, 0, stream>>>(aa);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   MLA_TRACE(3);
 
   MLA_TRACE(4);
-  combine_kernel<<<dim3(H, B, 2), 256, 0, stream>>>(part_o, part_ml, d.cache_lens, olat, H,
-                                                  p.max_seq_len, p.topk, plan.num_splits,
-                                                  plan.chunk_rows);
+  combine_kernel<<<dim3(H, B, 2), 256, 0, stream>>>(part_o, part_ml, wcum, olat, H);
   if ((err = hipGetLastError()) != hipSuccess) return err;
   MLA_TRACE(5);
 

@@ -9,18 +9,28 @@
 
 namespace mla {
 
-// MI355X: 256 compute units in 8 XCDs.  The split count targets a few
-// workgroups per CU; it is a design constant so the plan stays host-only.
+// MI355X: 256 compute units in 8 XCDs.  The attention kernel runs at most one
+// workgroup per CU (its LDS ring takes most of the 160 KB) and the plan aims
+// for one round of them; a design constant so the plan stays host-only.
 constexpr int kTargetCUs = 256;
-constexpr int kTileRows = 32;      // cache rows per LDS tile of the attention kernel
-constexpr int kMinChunkRows = 64;  // smallest split-T chunk
+constexpr int kTileRows = 32;           // cache rows per LDS tile of the attention kernel
+constexpr int kMaxTopkGroupTiles = 32;  // top-k: tiles per workgroup (index staging bound)
 
+// Work split of the attention kernel.  Sequence b has t_b tiles of 32
+// selected entries.  For a tile budget S, sequence b gets k_b = ceil(t_b / S)
+// workgroups, and workgroup i = w_b + p (w_b = k_0 + ... + k_{b-1}) takes its
+// tiles [floor(p t_b / k_b), floor((p+1) t_b / k_b)) and writes its partial
+// (O, m, l) into slot i.  S is the smallest budget with sum k_b <= 256 (one
+// round), at least min_group_tiles, and at most 32 with a top-k selection.
+// The lengths live on the device, so w_b and S are computed there; the sizes
+// here are upper bounds.
 struct DecodePlan {
-  int heads_padded;  // H rounded up to a multiple of 32 (one 32-head block per wave)
-  int head_blocks;   // heads_padded / 32
-  int chunk_rows;    // rows of the selection handled by one split (multiple of 32)
-  int num_splits;    // splits per sequence (upper bound; the kernels skip empty ones)
-  size_t off_qt, off_part_o, off_part_ml, off_olat, bytes;
+  int heads_padded;     // H rounded up to a multiple of 32 (one 32-head block per wave)
+  int head_blocks;      // heads_padded / 32
+  long long max_groups; // attention grid (upper bound of sum k_b)
+  int min_group_tiles;  // lower bound of S
+  long long max_tiles;  // tiles of the longest possible selection
+  size_t off_qt, off_part_o, off_part_ml, off_olat, off_wcum, off_wg_seq, bytes;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -31,24 +41,27 @@ inline DecodePlan make_decode_plan(const mla_params& p) {
   d.heads_padded = (H + 31) / 32 * 32;
   d.head_blocks = d.heads_padded / 32;
   const long long n_max = p.topk > 0 ? p.topk : p.max_seq_len;
-  const long long rows_total = (long long)B * n_max;
-  const long long target_groups = 2LL * kTargetCUs;
-  long long chunk = (rows_total + target_groups - 1) / target_groups;
-  chunk = (chunk + kTileRows - 1) / kTileRows * kTileRows;
-  if (chunk < kMinChunkRows) chunk = kMinChunkRows;
-  const long long n_cap = (n_max + kTileRows - 1) / kTileRows * kTileRows;
-  if (chunk > n_cap) chunk = n_cap > 0 ? n_cap : kTileRows;
-  d.chunk_rows = (int)chunk;
-  d.num_splits = n_max > 0 ? (int)((n_max + chunk - 1) / chunk) : 1;
+  d.max_tiles = (n_max + kTileRows - 1) / kTileRows;
+  d.min_group_tiles = 1;
+  long long G = B > kTargetCUs ? B : kTargetCUs;
+  if (p.topk > 0) {
+    const long long capped = (long long)B * ((d.max_tiles + kMaxTopkGroupTiles - 1) / kMaxTopkGroupTiles);
+    if (G < capped) G = capped;
+  }
+  d.max_groups = G;
   size_t off = 0;
-  d.off_qt = off;
+  d.off_qt = off;  // bf16 [B][heads_padded][576]
   off = align256(off + (size_t)B * d.heads_padded * 576 * 2);
-  d.off_part_o = off;  // bf16 [B][H][num_splits][512]
-  off = align256(off + (size_t)B * d.num_splits * H * 512 * 2);
-  d.off_part_ml = off;  // fp32 [B][H][num_splits][2]
-  off = align256(off + (size_t)B * d.num_splits * H * 2 * 4);
-  d.off_olat = off;
+  d.off_part_o = off;  // bf16 [max_groups][H][512]
+  off = align256(off + (size_t)G * H * 512 * 2);
+  d.off_part_ml = off;  // fp32 [max_groups][H][2]
+  off = align256(off + (size_t)G * H * 2 * 4);
+  d.off_olat = off;  // bf16 [B][H][512]
   off = align256(off + (size_t)B * H * 512 * 2);
+  d.off_wcum = off;  // int32 [B + 1]: w_b, w_B = workgroups in use
+  off = align256(off + ((size_t)B + 1) * 4);
+  d.off_wg_seq = off;  // int32 [max_groups]
+  off = align256(off + (size_t)G * 4);
   d.bytes = off;
   return d;
 }

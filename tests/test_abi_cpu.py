@@ -114,7 +114,11 @@ def test_workspace_size_is_host_only_and_monotone(m):
         p = m.make_params(8, 128, T)
         sizes.append(m.decode_workspace_size(p))
     assert all(s > 0 for s in sizes) and sizes == sorted(sizes)
-    # top-k bounds the work by k, not by the buffer
-    assert m.decode_workspace_size(m.make_params(8, 128, 65536, topk=2048)) < sizes[-1]
+    # partials: one per attention workgroup, at most max(256, B) of them for a
+    # dense selection whatever the buffer length; a top-k selection of more
+    # than 32 tiles per workgroup needs more workgroups
+    assert m.decode_workspace_size(m.make_params(512, 128, 4096)) > sizes[1]
+    small_k = m.decode_workspace_size(m.make_params(8, 128, 65536, topk=2048))
+    assert m.decode_workspace_size(m.make_params(8, 128, 65536, topk=65536)) > small_k
     with pytest.raises(m.MLAError):
         m.decode_workspace_size(m.make_params(8, 200, 4096))
