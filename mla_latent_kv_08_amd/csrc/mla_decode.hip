@@ -239,7 +239,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
 // read, and the 4 rows x 4 chunks of a transposing read, on distinct banks.
 // ---------------------------------------------------------------------------
 constexpr int kTT = kTileRows;              // rows per tile
-constexpr int kStages = 2;                  // tiles in the LDS ring
+constexpr int kStages = 3;                  // tiles in the LDS ring
 constexpr int kTileElems = kTT * kQK;       // bf16 elements per tile (36 KB)
 constexpr int kMaxIdx = kMaxTopkGroupTiles * kTT;  // top-k entries staged per workgroup
 constexpr int kAttnWaves = 4;
@@ -301,6 +301,10 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
     asm volatile("s_barrier" ::: "memory");                         \
   } while (0)
 
+// Lambdas of the attention kernel carry accumulators by reference: they must
+// be inlined, or those live in scratch memory.
+#define MLA_INLINE __attribute__((always_inline))
+
 template <int S>
 struct Stage {
   static constexpr int value = S;
@@ -327,27 +331,32 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   // is a compile-time constant in the loop body below.
   __shared__ __attribute__((aligned(16))) uint16_t sT0[kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t sT1[kTileElems];
-  __shared__ __attribute__((aligned(16))) uint16_t sP[128 * kPStride];
-  __shared__ float sAlpha[128];
+  __shared__ __attribute__((aligned(16))) uint16_t sT2[kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t sP[2 * 128 * kPStride];  // by tile parity
+  __shared__ float sAlpha[2 * 128];                                          // by tile parity
   __shared__ float sL[128];
   __shared__ uint32_t sMask[kStages];
-  __shared__ uint32_t sRescale[2];  // per tile parity: some head of the tile rescales
+  __shared__ uint32_t sRescale[3];  // by tile mod 3: some head of the tile rescales
   __shared__ int sIdx[TOPK ? kMaxIdx : 1];
-  static_assert(kStages == 2, "one LDS array per ring slot");
-  auto slot = [&](auto S) -> uint16_t* {
+  static_assert(kStages == 3, "one LDS array per ring slot");
+  auto slot = [&](auto S) MLA_INLINE -> uint16_t* {
     constexpr int st = decltype(S)::value;
     if constexpr (st == 0) return sT0;
-    else return sT1;
+    else if constexpr (st == 1) return sT1;
+    else return sT2;
   };
 
   const bool active = wave < a.head_blocks;  // this wave has score heads
   const int n = lane & 31, g = lane >> 5;
   const int head = wave * 32 + n;
 
-  // P rows and l of heads without a score wave stay zero; their alpha stays 1
-  for (int i = tid; i < 128 * kPStride / 2; i += kAttnThreads) ((uint32_t*)sP)[i] = 0u;
+  // P rows and l of heads without a score wave stay zero; their alpha stays 1.
+  // Slot 2 and P buffer 1 stand in for "tile -1" of the pipeline: zero.
+  for (int i = tid; i < 2 * 128 * kPStride / 2; i += kAttnThreads) ((uint32_t*)sP)[i] = 0u;
+  for (int i = tid; i < kTileElems / 8; i += kAttnThreads) ((u32x4*)sT2)[i] = u32x4{0u, 0u, 0u, 0u};
   if (tid < 128) {
     sAlpha[tid] = 1.f;
+    sAlpha[128 + tid] = 1.f;
     sL[tid] = 0.f;
   }
 
@@ -378,12 +387,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
       sIdx[i] = (r >= 0 && r < len) ? r : -1;
     }
   }
-  if (tid < 2) sRescale[tid] = 0u;
+  if (tid < 3) sRescale[tid] = 0u;
   __syncthreads();
 
   // Row of tile position t (any valid row when the position selects
   // nothing: its score is masked, and it must only be finite).
-  auto tile_row = [&](int pt, int t) -> int {
+  auto tile_row = [&](int pt, int t) MLA_INLINE -> int {
     const int pos = pt + t;
     if (TOPK) {
       const int r = pos < p1 ? sIdx[pos - p0] : -1;
@@ -392,7 +401,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     return pos < p1 ? pos : p1 - 1;
   };
   // Bit t of a tile's mask: tile row t selects a position.
-  auto publish_mask = [&](int pt, int stage) {
+  auto publish_mask = [&](int pt, int stage) MLA_INLINE {
     if (TOPK) {
       if (wave == 0) {
         const int pos = pt + lane;
@@ -413,7 +422,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   struct DmaCursor {
     int t, phys;
   };
-  auto dma_start = [&]() -> DmaCursor {
+  auto dma_start = [&]() MLA_INLINE -> DmaCursor {
     int P = 64 * wave + lane;
     asm volatile("" : "+v"(P));  // recomputed per tile, not kept live
     const int t = P / 72;
@@ -421,12 +430,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   };
   // base: LDS byte address of the tile slot plus 1024 * wave, laundered so
   // the compiler keeps one value per tile instead of nine per slot.
-  auto dma_base = [&](uint16_t* dst) -> uint32_t {
+  auto dma_base = [&](uint16_t* dst) MLA_INLINE -> uint32_t {
     uint32_t base = lds_addr(dst) + 1024u * wave;
     asm volatile("" : "+s"(base));
     return base;
   };
-  auto dma_step = [&](DmaCursor& c, int pt, uint32_t base, auto K) {
+  auto dma_step = [&](DmaCursor& c, int pt, uint32_t base, auto K) MLA_INLINE {
     constexpr int k = decltype(K)::value;
     const int ch = c.phys ^ swz(c.t);
     const size_t row = seq_row0 + tile_row(pt, c.t);
@@ -440,7 +449,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
       c.t += 1;
     }
   };
-  auto dma_all = [&](DmaCursor& c, int pt, uint32_t base) {
+  auto dma_all = [&](DmaCursor& c, int pt, uint32_t base) MLA_INLINE {
     dma_step(c, pt, base, Stage<0>{});
     dma_step(c, pt, base, Stage<1>{});
     dma_step(c, pt, base, Stage<2>{});
@@ -451,19 +460,81 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     dma_step(c, pt, base, Stage<7>{});
     dma_step(c, pt, base, Stage<8>{});
   };
-  auto issue_bf16 = [&](int j, auto S) {
+  auto issue_bf16 = [&](int j, auto S) MLA_INLINE {
     const int pt = p0 + j * kTT;
     DmaCursor c = dma_start();
     const uint32_t base = dma_base(slot(S));
     dma_all(c, pt, base);
     publish_mask(pt, decltype(S)::value);
   };
+  // Fast path for a dense tile of 32 selected rows: the rows are consecutive,
+  // so each of a lane's nine loads sits at a fixed byte offset from the tile's
+  // first latent or rotary row.  Offsets are 16-bit (latent t*1024 + ch*16 <
+  // 32768, rotary t*128 + (ch-64)*16 with bit 15 set), two per register,
+  // computed once; a load then costs a select and a 64-bit add instead of
+  // the row / chunk / swizzle arithmetic.
+  uint32_t doff[5] = {0u, 0u, 0u, 0u, 0u};
+  if (!FP8 && !TOPK) {
+    DmaCursor c = dma_start();
+    auto put = [&](auto K) MLA_INLINE {  // explicit steps: doff is only indexed by constants
+      constexpr int k = decltype(K)::value;
+      const int ch = c.phys ^ swz(c.t);
+      const uint32_t off = ch < 64 ? (uint32_t)(c.t * 1024 + ch * 16) : (uint32_t)(c.t * 128 + (ch - 64) * 16) | 0x8000u;
+      doff[k >> 1] |= off << (16 * (k & 1));
+      c.phys += 40;
+      c.t += 3;
+      if (c.phys >= 72) {
+        c.phys -= 72;
+        c.t += 1;
+      }
+    };
+    put(Stage<0>{});
+    put(Stage<1>{});
+    put(Stage<2>{});
+    put(Stage<3>{});
+    put(Stage<4>{});
+    put(Stage<5>{});
+    put(Stage<6>{});
+    put(Stage<7>{});
+    put(Stage<8>{});
+  }
+  struct FullTile {
+    const char* kv;
+    const char* pe;
+    uint32_t base;
+  };
+  auto full_tile = [&](int j, auto S) MLA_INLINE -> FullTile {
+    const int pt = p0 + j * kTT;
+    return FullTile{(const char*)a.kv + (seq_row0 + pt) * (size_t)(kC * 2),
+                    (const char*)a.pe + (seq_row0 + pt) * (size_t)(kR * 2), dma_base(slot(S))};
+  };
+  auto full_load = [&](const FullTile& ft, auto K) MLA_INLINE {
+    constexpr int k = decltype(K)::value;
+    uint32_t d = doff[k >> 1];
+    asm volatile("" : "+v"(d));  // unpacked here, not kept as nine 64-bit offsets
+    const uint32_t o = (d >> (16 * (k & 1))) & 0xFFFFu;
+    const char* pe_row = ft.pe;  // select values, not struct members (keeps ft in registers)
+    const char* kv_row = ft.kv;
+    const char* src = ((o & 0x8000u) ? pe_row : kv_row) + (o & 0x7FFFu);
+    lds_dma16<4096 * k>(src, ft.base);
+  };
+  auto full_all = [&](const FullTile& ft) MLA_INLINE {
+    full_load(ft, Stage<0>{});
+    full_load(ft, Stage<1>{});
+    full_load(ft, Stage<2>{});
+    full_load(ft, Stage<3>{});
+    full_load(ft, Stage<4>{});
+    full_load(ft, Stage<5>{});
+    full_load(ft, Stage<6>{});
+    full_load(ft, Stage<7>{});
+    full_load(ft, Stage<8>{});
+  };
 
   // ---- FP8 tiles through registers: 4 units of 16 codes + 1 rotary chunk per thread
   u32x4 c8[FP8 ? 4 : 1];
   float csc[FP8 ? 4 : 1];
   u32x4 pev;
-  auto load_fp8 = [&](int j) {
+  auto load_fp8 = [&](int j) MLA_INLINE {
     const int pt = p0 + j * kTT;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -475,7 +546,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     const size_t row = seq_row0 + tile_row(pt, tid >> 3);
     pev = *(const u32x4*)(a.pe + row * kR + (tid & 7) * 8);
   };
-  auto store_fp8 = [&](int j, auto S) {
+  auto store_fp8 = [&](int j, auto S) MLA_INLINE {
     const int stage = decltype(S)::value;
     uint16_t* dst = slot(S);
 #pragma unroll
@@ -521,23 +592,167 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   MLA_WAIT_VMCNT(0);
   if (FP8) store_fp8(0, Stage<0>{});
 
+  // ---- software pipeline over the tiles, one workgroup barrier per tile.
+  // Body j: barrier; loads of tile j+1 (slot of tile j-2); scores of tile j;
+  // then the update with tile j-1 (its P, the rescale by its alpha) with the
+  // softmax of tile j interleaved, so the VALU work of the softmax runs while
+  // the matrix cores work on the update.  P and alpha are double-buffered by
+  // tile parity and the rescale flags cycle over three tiles: each is written
+  // in body j, read in body j+1 and cleared in body j+2, with a barrier
+  // between every two of these.
+  auto pbuf = [&](int jj) MLA_INLINE -> uint16_t* { return sP + (jj & 1) * (128 * kPStride); };
+  auto rescale = [&](int jj) MLA_INLINE {
+    if (sRescale[(jj + 3) % 3]) {  // rare: some head's running max moved
+      const float* al_src = sAlpha + (jj & 1) * 128;
+      float al[4];
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) al[nb] = al_src[32 * nb + n];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        f32x16 tcopy = o[i];
+        asm volatile("" : "+v"(tcopy));  // scale a copy; o[i] itself stays an MFMA value
+        o[i] = mfma32(zq, zq, tcopy * al[i & 3]);
+      }
+    }
+  };
+  // Update step (u, m): A = 2 transposing reads of tile pt (rows 16u + 4g + r
+  // and 16u + 8 + 4g + r), B = P^T of head block nb (pb, 16 bytes per lane).
+  auto tr_read = [&](const uint16_t* pt, int u, int m) MLA_INLINE -> u32x4 {
+    const uint16_t* base = pt + 16 * u * kQK + 64 * (m >> 1);
+    const u32x2 v0 = ds_read_tr16(base + tr_base[0][m & 1]);
+    const u32x2 v1 = ds_read_tr16(base + tr_base[1][m & 1]);
+    return u32x4{v0[0], v0[1], v1[0], v1[1]};
+  };
+  auto pv_mfma = [&](const u32x4& va, const u32x4 (&pb)[4], int m) MLA_INLINE {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) o[4 * m + nb] = mfma32(va, pb[nb], o[4 * m + nb]);
+  };
+  auto pb_read = [&](const uint16_t* pp, u32x4 (&pb)[4], int u) MLA_INLINE {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) pb[nb] = *(const u32x4*)(pp + (32 * nb + n) * kPStride + 16 * u + 8 * g);
+  };
+  // Update with tile jp interleaved with the softmax of tile j held in s:
+  // eight scheduling regions, each with the four MFMAs of one update step
+  // (whose A operand was read one region earlier) and a slice of the softmax.
+  auto update_softmax = [&](const uint16_t* ptile, int jp, f32x16& s, int j, uint32_t mask) MLA_INLINE {
+    const uint16_t* pp = pbuf(jp);
+    u32x4 pb[4], va[3];
+    float mx, m_use, m_sub, alpha;
+    pb_read(pp, pb, 0);
+    va[0] = tr_read(ptile, 0, 0);
+    va[1] = tr_read(ptile, 0, 1);
+    // region 0 (A operands are read two steps ahead of their MFMAs)
+    va[2] = tr_read(ptile, 0, 2);
+    pv_mfma(va[0], pb, 0);
+    if (mask != 0xFFFFFFFFu) {  // partial tile (wave-uniform branch)
+      const uint32_t ml = (mask >> (4 * g)) & 0x0F0F0F0Fu;  // rows 8a + 4g + b -> bit 8a + b
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (!((ml >> (8 * (e >> 2) + (e & 3))) & 1u)) s[e] = -INFINITY;
+    }
+    mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    __builtin_amdgcn_sched_barrier(0);
+    // region 1: the other 16 rows of this lane's head sit in lane l ^ 32
+    va[0] = tr_read(ptile, 0, 3);
+    pv_mfma(va[1], pb, 1);
+    mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
+                         fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // region 2: online softmax in log2 units; the running max only moves when
+    // the new one exceeds it by more than 8 (probabilities stay <= 2^8), which
+    // skips most rescales of O without changing the result
+    va[1] = tr_read(ptile, 1, 0);
+    pv_mfma(va[2], pb, 2);
+    {
+      const float mt = mx * a.scale_log2;
+      m_use = (m_run == -INFINITY || mt > m_run + 8.0f) ? fmaxf(mt, m_run) : m_run;
+      m_sub = (m_use == -INFINITY) ? 0.f : m_use;
+      alpha = (m_use == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_use);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], a.scale_log2, -m_sub));
+    __builtin_amdgcn_sched_barrier(0);
+    // region 3 (then the B operand of the second k-step)
+    va[2] = tr_read(ptile, 1, 1);
+    pv_mfma(va[0], pb, 3);
+#pragma unroll
+    for (int e = 4; e < 8; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], a.scale_log2, -m_sub));
+    pb_read(pp, pb, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // region 4
+    va[0] = tr_read(ptile, 1, 2);
+    pv_mfma(va[1], pb, 0);
+#pragma unroll
+    for (int e = 8; e < 12; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], a.scale_log2, -m_sub));
+    __builtin_amdgcn_sched_barrier(0);
+    // region 5
+    va[1] = tr_read(ptile, 1, 3);
+    pv_mfma(va[2], pb, 1);
+#pragma unroll
+    for (int e = 12; e < 16; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], a.scale_log2, -m_sub));
+    const float lsum = (((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]))) +
+                       (((s[8] + s[9]) + (s[10] + s[11])) + ((s[12] + s[13]) + (s[14] + s[15])));
+    __builtin_amdgcn_sched_barrier(0);
+    // region 6: P rows 8a + 4g + b land at tau = 16(a>>1) + 8g + 4(a&1) + b:
+    // two contiguous 16-byte pieces per lane
+    pv_mfma(va[0], pb, 2);
+    l_run = l_run * alpha + lsum;
+    m_run = m_use;
+    if (active) {  // waves without score heads leave their (zero) P rows alone
+      uint16_t* prow = pbuf(j) + head * kPStride + 8 * g;
+      *(u32x4*)(prow) = u32x4{cvt_pk_bf16(s[0], s[1]), cvt_pk_bf16(s[2], s[3]),
+                              cvt_pk_bf16(s[4], s[5]), cvt_pk_bf16(s[6], s[7])};
+      *(u32x4*)(prow + 16) = u32x4{cvt_pk_bf16(s[8], s[9]), cvt_pk_bf16(s[10], s[11]),
+                                   cvt_pk_bf16(s[12], s[13]), cvt_pk_bf16(s[14], s[15])};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // region 7
+    pv_mfma(va[1], pb, 3);
+    if (active) {
+      if (g == 0) sAlpha[(j & 1) * 128 + head] = alpha;
+      if (alpha != 1.f) sRescale[j % 3] = 1u;  // benign race: every writer stores 1
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The update alone (after the last tile).
+  auto update_only = [&](const uint16_t* ptile, int jp) MLA_INLINE {
+    const uint16_t* pp = pbuf(jp);
+    u32x4 pb[4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      pb_read(pp, pb, u);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) pv_mfma(tr_read(ptile, u, m), pb, m);
+    }
+  };
+
   // Tile j lives in ring slot S = j % kStages (a compile-time constant here).
-  auto body = [&](int j, auto S) {
+  auto body = [&](int j, auto S) MLA_INLINE {
     constexpr int st = decltype(S)::value;
-    constexpr int s1 = (st + 1) % kStages;  // slot of tile j + 1 (held tile j - 1)
-    // Barrier A: tile j visible to every wave (the bf16 path first waits for
-    // its own loads of it); every wave is done with tile j-1 and with sP.
+    constexpr int s1 = (st + 1) % kStages;  // slot of tile j + 1 (held tile j - 2)
+    constexpr int sp = (st + 2) % kStages;  // slot of tile j - 1
+    // Barrier: tile j visible to every wave (the bf16 path first waits for its
+    // own loads of it); P, alpha and flag of tile j-1 visible; every wave is
+    // done with tile j-2 and with the P buffer and flag the softmax of tile j
+    // is about to write.
     if (!FP8) MLA_WAIT_VMCNT(0);
     MLA_LDS_BARRIER();
-    const bool issue = !FP8 && j + 1 < ntiles;
-    const int pt_next = p0 + (j + 1) * kTT;
-    DmaCursor cur = dma_start();
-    const uint32_t nbase = dma_base(slot(Stage<s1>{}));
-    if (issue) publish_mask(pt_next, s1);
-    if (FP8 && j + 1 < ntiles) load_fp8(j + 1);
-    // every wave has passed barrier A, so is done with the previous tile's flag
-    if (tid == 0) sRescale[(j + 1) & 1] = 0u;
+    // tile j+1: a full dense tile is loaded by the fast path, its nine loads
+    // per thread spread over the score MFMAs; any other tile in one burst here
+    const bool fast = !FP8 && !TOPK && j + 1 < ntiles && p0 + (j + 2) * kTT <= p1;
+    const FullTile ft = full_tile(j + 1, Stage<s1>{});
+    if (j + 1 < ntiles) {
+      if (FP8) load_fp8(j + 1);
+      else if (fast) publish_mask(p0 + (j + 1) * kTT, s1);
+      else issue_bf16(j + 1, Stage<s1>{});
+    }
+    if (tid == 0) sRescale[(j + 1) % 3] = 0u;  // flag of tile j-2: read in body j-1
     const uint16_t* tile = slot(S);
+    f32x16 s = {};  // waves without score heads run the softmax on zeros
     if (active) {
       // Scores.  The 36 MFMAs accumulate in VGPRs (inline asm: the compiler
       // would put this accumulator in AGPRs, where O already takes all 256).
@@ -545,24 +760,29 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
       // need no wait states; the s_nop after the chain covers the MFMA-write
       // -> VALU-read hazard (>= 18 wait states for this 8-pass instruction).
       // Operand reads run four k-steps ahead of the MFMAs.
-      f32x16 s;
       u32x4 ka[5];
 #pragma unroll
       for (int k = 0; k < 4; ++k) ka[k] = *(const u32x4*)(tile + sc_base[k & 3] + 64 * (k >> 2));
-      // nine explicitly instantiated groups of four k-steps, one load of tile
-      // j+1 in each (keeps the chain fully unrolled with the loads inside)
-      auto group = [&](auto Q) {
-        constexpr int q = decltype(Q)::value;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int k = 4 * q + kk;
-          if (k + 4 < 36) ka[(k + 4) % 5] = *(const u32x4*)(tile + sc_base[(k + 4) & 3] + 64 * ((k + 4) >> 2));
-          if (k == 0)
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(ka[0]), "v"(qreg[0]));
-          else
-            asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(ka[k % 5]), "v"(qreg[k]));
-          if (kk == 1 && issue) dma_step(cur, pt_next, nbase, Q);
+      // nine explicitly instantiated groups of four k-steps (keeps the chain
+      // fully unrolled, so qreg is indexed by constants)
+      auto step = [&](auto Q, auto KK) MLA_INLINE {
+        constexpr int kk = decltype(KK)::value;
+        constexpr int k = 4 * decltype(Q)::value + kk;
+        if constexpr (k + 4 < 36) ka[(k + 4) % 5] = *(const u32x4*)(tile + sc_base[(k + 4) & 3] + 64 * ((k + 4) >> 2));
+        if constexpr (k == 0)
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(ka[0]), "v"(qreg[0]));
+        else
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(ka[k % 5]), "v"(qreg[k]));
+        if constexpr (kk == 1) {
+          if (fast) full_load(ft, Q);
         }
+        if constexpr (k == 35) asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s));
+      };
+      auto group = [&](auto Q) MLA_INLINE {
+        step(Q, Stage<0>{});
+        step(Q, Stage<1>{});
+        step(Q, Stage<2>{});
+        step(Q, Stage<3>{});
       };
       group(Stage<0>{});
       group(Stage<1>{});
@@ -573,85 +793,36 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
       group(Stage<6>{});
       group(Stage<7>{});
       group(Stage<8>{});
-      asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s));
-      const uint32_t mask = sMask[st];
-      if (mask != 0xFFFFFFFFu) {  // partial tile (wave-uniform branch)
-        const uint32_t ml = (mask >> (4 * g)) & 0x0F0F0F0Fu;  // rows 8a + 4g + b -> bit 8a + b
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-          if (!((ml >> (8 * (e >> 2) + (e & 3))) & 1u)) s[e] = -INFINITY;
-      }
-      float mx = s[0];
-#pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // online softmax in log2 units; the running max only moves when the
-      // new one exceeds it by more than 8 (probabilities stay <= 2^8), which
-      // skips most rescales of O without changing the result
-      const float mt = mx * a.scale_log2;
-      const float m_use = (m_run == -INFINITY || mt > m_run + 8.0f) ? fmaxf(mt, m_run) : m_run;
-      const float m_sub = (m_use == -INFINITY) ? 0.f : m_use;
-      const float alpha = (m_use == m_run) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_use);
-      float lsum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], a.scale_log2, -m_sub));
-        lsum += s[e];
-      }
-      l_run = l_run * alpha + lsum;
-      m_run = m_use;
-      // P rows 8a + 4g + b land at tau = 16(a>>1) + 8g + 4(a&1) + b: two
-      // contiguous 16-byte pieces per lane
-      uint16_t* prow = sP + head * kPStride + 8 * g;
-      *(u32x4*)(prow) = u32x4{cvt_pk_bf16(s[0], s[1]), cvt_pk_bf16(s[2], s[3]),
-                              cvt_pk_bf16(s[4], s[5]), cvt_pk_bf16(s[6], s[7])};
-      *(u32x4*)(prow + 16) = u32x4{cvt_pk_bf16(s[8], s[9]), cvt_pk_bf16(s[10], s[11]),
-                                   cvt_pk_bf16(s[12], s[13]), cvt_pk_bf16(s[14], s[15])};
-      if (g == 0) sAlpha[head] = alpha;
-      if (alpha != 1.f) sRescale[j & 1] = 1u;  // benign race: every writer stores 1
-    } else if (issue) {
-      dma_all(cur, pt_next, nbase);
+    } else if (fast) {
+      full_all(ft);
     }
-    // Barrier B: all P (and rescale factors) of this tile are in LDS.
-    MLA_LDS_BARRIER();
-    if (sRescale[j & 1]) {  // rare: some head's running max moved
-      float al[4];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) al[nb] = sAlpha[32 * nb + n];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        f32x16 tcopy = o[i];
-        asm volatile("" : "+v"(tcopy));  // scale a copy; o[i] itself stays an MFMA value
-        o[i] = mfma32(zq, zq, tcopy * al[i & 3]);
-      }
-    }
-    // Update: column block m, k-step u: A = 2 transposing reads (rows
-    // 16u + 4g + r and 16u + 8 + 4g + r), B = P^T of head block nb (16 bytes).
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      u32x4 pb[4];
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) pb[nb] = *(const u32x4*)(sP + (32 * nb + n) * kPStride + 16 * u + 8 * g);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint16_t* base = tile + 16 * u * kQK + 64 * (m >> 1);
-        const u32x2 v0 = ds_read_tr16(base + tr_base[0][m & 1]);
-        const u32x2 v1 = ds_read_tr16(base + tr_base[1][m & 1]);
-        const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb) o[4 * m + nb] = mfma32(va, pb[nb], o[4 * m + nb]);
-      }
-    }
+    const uint32_t mask = sMask[st];
+    // one code path for every wave and tile (branches around the update would
+    // merge 256 accumulator registers): for j = 0 the update runs on the
+    // zeroed slot and P buffer of "tile -1"
+    rescale(j - 1);
+    update_softmax(slot(Stage<sp>{}), j - 1, s, j, mask);
     if (FP8 && j + 1 < ntiles) store_fp8(j + 1, Stage<s1>{});
   };
   for (int j0 = 0; j0 < ntiles; j0 += kStages) {
     body(j0, Stage<0>{});
     if (j0 + 1 < ntiles) body(j0 + 1, Stage<1>{});
+    if (j0 + 2 < ntiles) body(j0 + 2, Stage<2>{});
+  }
+  // drain: the update with the last tile
+  {
+    MLA_LDS_BARRIER();
+    const int jl = ntiles - 1;
+    rescale(jl);
+    const int sl = jl % kStages;
+    const uint16_t* lt = sl == 0 ? slot(Stage<0>{}) : (sl == 1 ? slot(Stage<1>{}) : slot(Stage<2>{}));
+    update_only(lt, jl);
   }
 
   // ---- partial result: (m, l) in fp32 and O / l in bf16,
-  // staged through the idle ring (head blocks 0-1, then 2-3, in slots 0-1;
-  // rows of kOStride) so that every head's 512 values leave as one 1 KB row.
+  // staged through the idle ring (head blocks 0-2 in slots 0-2, then block 3
+  // in slot 0; rows of kOStride) so that every head's 512 values leave as one
+  // 1 KB row.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
   if (active && g == 0) {
     sL[head] = l_tot;
@@ -662,7 +833,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     }
   }
   __syncthreads();  // ring idle, sL complete
-  auto stage_out = [&](auto NB, auto SL) {
+  auto stage_out = [&](auto NB, auto SL) MLA_INLINE {
     constexpr int nb = decltype(NB)::value;
     const float lt = sL[32 * nb + n];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
@@ -678,9 +849,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   };
   stage_out(Stage<0>{}, Stage<0>{});
   stage_out(Stage<1>{}, Stage<1>{});
+  stage_out(Stage<2>{}, Stage<2>{});
   __syncthreads();
   uint16_t* dst = a.part_o + slot_id * a.H * kC;
-  auto copy_out = [&](auto NB, auto SL) {
+  auto copy_out = [&](auto NB, auto SL) MLA_INLINE {
     constexpr int nb = decltype(NB)::value;
     const uint16_t* srcb = slot(SL);
 #pragma unroll 2
@@ -691,13 +863,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   };
   copy_out(Stage<0>{}, Stage<0>{});
   copy_out(Stage<1>{}, Stage<1>{});
-  if (a.H > 64) {  // head blocks 2 and 3 (uniform branch)
+  copy_out(Stage<2>{}, Stage<2>{});
+  if (a.H > 96) {  // head block 3 through slot 0 (uniform branch)
     __syncthreads();
-    stage_out(Stage<2>{}, Stage<0>{});
-    stage_out(Stage<3>{}, Stage<1>{});
+    stage_out(Stage<3>{}, Stage<0>{});
     __syncthreads();
-    copy_out(Stage<2>{}, Stage<0>{});
-    copy_out(Stage<3>{}, Stage<1>{});
+    copy_out(Stage<3>{}, Stage<0>{});
   }
 }
 
