@@ -11,11 +11,12 @@ of a real model do not share weights or caches either).
 
 Timing: each replica's step is captured once in a HIP graph; the timed region
 replays K steps, bracketed by torch.cuda.synchronize().  Per-kernel durations
-come from a second pass of K eager steps with HIP events recorded around
-every kernel on the library's stream (the queue is pre-filled behind a fixed
-GPU sleep so the events time the kernels, not host launch latency).  The
-dominant kernel's average duration gives the roofline entry.  The CPU
-baseline times the oracle on a bounded sample of the same workload.
+come from a second pass of K eager steps in which the library launches every
+kernel with start/end HIP events stamped by the dispatch itself (the
+mla_params trace_events hook), i.e. the same kernel start and end times a
+kernel trace reports.  The dominant kernel's average duration gives the
+roofline entry.  The CPU baseline times the oracle on a bounded sample of the
+same workload.
 
 Prints one JSON line.
 """
@@ -65,6 +66,45 @@ class HipEvents:
     def destroy(self, evs):
         for e in evs:
             self.hip.hipEventDestroy(e)
+
+
+def sources_sha():
+    """sha256 (16 hex digits) of the kernel sources, in the order `cat *.hip *.hpp` reads them."""
+    import glob
+    import hashlib
+    d = os.path.join(ROOT, "mla_latent_kv_08_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(d, "*.hip"))) + sorted(glob.glob(os.path.join(d, "*.hpp"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload, kernel_symbol):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary,
+    or None when there is none for this kernel or the sources changed since."""
+    import re
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"Sources at sha256 \(csrc/\*\.hip, \*\.hpp\) `([0-9a-f]+)`", text)
+    if not m or m.group(1) != sources_sha():
+        return None
+    for line in text.splitlines():
+        cells = [c.strip().strip("`") for c in line.strip().strip("|").split("|")]
+        if len(cells) == 6 and cells[0] == workload and cells[1] == kernel_symbol:
+            return int(float(cells[5]))
+    return None
+
+
+def kernel_symbol(name, w):
+    if name == "attention":
+        return "mla::attn_kernel<%s, %s>" % ("true" if w.fp8 else "false", "true" if w.topk else "false")
+    if name == "cache_write":
+        return "mla::cache_write_fp8_kernel" if w.fp8 else "mla::cache_write_bf16_kernel"
+    return {"absorb": "mla::absorb_kernel", "combine": "mla::combine_kernel",
+            "uproj": "mla::uproj_kernel"}[name]
 
 
 def workload_bytes_flops(w, lens, k):
@@ -165,6 +205,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches, not graph replay")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run 5 plain device copies of BYTES bytes (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
@@ -173,6 +216,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = args.copy_calibration // 16 * 16
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
+        return
 
     from mla_latent_kv_08_amd import mla, synth
 
@@ -223,14 +276,15 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = 1e3 * elapsed / args.steps
 
-    # ---- per-kernel durations: eager steps with HIP events around every kernel
+    # ---- per-kernel durations: eager steps, start/end of every kernel stamped
+    # by its dispatch
     hev = HipEvents()
     ev = hev.create(10 * args.steps)
     traces = []
     for i in range(args.steps):
         e = ev[10 * i: 10 * i + 10]
         traces.append(((ctypes.c_void_p * 2)(*e[:2]), (ctypes.c_void_p * 8)(*e[2:])))
-    torch.cuda._sleep(int(2e8))  # hold the queue while the host enqueues the steps
+    torch.cuda._sleep(int(2e8))  # let the host enqueue the steps ahead of the GPU
     for i in range(args.steps):
         step(mla, reps[i % R], shared, out, ws,
              trace=(ctypes.addressof(traces[i][0]), ctypes.addressof(traces[i][1])))
@@ -253,7 +307,7 @@ def main():
         roof = {"bound": "mfma", "achieved": kf / t_dom / 1e12, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = counter_traffic(w.name, kernel_symbol(dom, w))
     roof["kernel"] = dom
     roof["avg_us"] = avg_us[dom]
 
@@ -285,6 +339,7 @@ def main():
         "step_hbm_frac": total_bytes / step_s / 1e9 / PEAK_HBM_GBS,
         "step_mfma_frac": total_flops / step_s / 1e12 / PEAK_BF16_TFLOPS,
         "kernel_avg_us": avg_us,
+        "kernel_timing": "dispatch-stamped HIP events, eager pass of the same K steps",
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -73,11 +73,13 @@ typedef enum mla_kv_dtype {
  *   softmax_scale multiplier of the logits, finite and > 0 (1/sqrt(192) for
  *                 DeepSeek-V3; a YaRN correction is folded in by the caller)
  *   trace_events  optional instrumentation, normally NULL.  Otherwise an array
- *                 of hipEvent_t (as void*): mla_decode records events[2k] and
- *                 events[2k+1] on `stream` around its k-th kernel
- *                 (k = 0 absorb, 1 attention, 2 combine, 3 up-projection;
- *                 8 events); mla_cache_write records events[0] and events[1]
- *                 around its kernel.
+ *                 of hipEvent_t (as void*, created with timing enabled):
+ *                 events[2k] and events[2k+1] receive the start and end time
+ *                 of mla_decode's k-th kernel (k = 0 absorb, 1 attention,
+ *                 2 combine, 3 up-projection; 8 events), stamped by the kernel
+ *                 dispatch itself (hipExtLaunchKernel), so their elapsed time
+ *                 is the kernel's duration; mla_cache_write uses events[0]
+ *                 and events[1] for its kernel.
  */
 typedef struct mla_params {
   int32_t batch;

@@ -61,25 +61,19 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(
 
 hipError_t launch_cache_write(const mla_params& p, const CacheWriteArgs& c, hipStream_t stream) {
   const int B = p.batch, s = p.seqlen_q, T = p.max_seq_len;
-  hipEvent_t* ev = (hipEvent_t*)p.trace_events;
-  hipError_t err;
-  if (ev && (err = hipEventRecord(ev[0], stream)) != hipSuccess) return err;
+  hipEvent_t const* ev = (hipEvent_t const*)p.trace_events;
   if (p.kv_dtype == MLA_KV_FP8_E4M3_B128) {
     const long long waves = (long long)B * s * 4;
     const unsigned blocks = (unsigned)((waves + 3) / 4);
-    cache_write_fp8_kernel<<<blocks, 256, 0, stream>>>(
-        (const uint16_t*)c.kv_new, (const uint16_t*)c.pe_new, c.start_pos, (uint8_t*)c.kv_cache,
-        c.kv_scale, (uint16_t*)c.pe_cache, B, s, T);
-  } else {
-    const long long threads = (long long)B * s * 72;
-    const unsigned blocks = (unsigned)((threads + 255) / 256);
-    cache_write_bf16_kernel<<<blocks, 256, 0, stream>>>(
-        (const uint16_t*)c.kv_new, (const uint16_t*)c.pe_new, c.start_pos,
-        (uint16_t*)c.kv_cache, (uint16_t*)c.pe_cache, B, s, T);
+    return launch_kernel(cache_write_fp8_kernel, dim3(blocks), dim3(256), stream, ev,
+                         (const uint16_t*)c.kv_new, (const uint16_t*)c.pe_new, c.start_pos,
+                         (uint8_t*)c.kv_cache, c.kv_scale, (uint16_t*)c.pe_cache, B, s, T);
   }
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  if (ev && (err = hipEventRecord(ev[1], stream)) != hipSuccess) return err;
-  return hipSuccess;
+  const long long threads = (long long)B * s * 72;
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
+  return launch_kernel(cache_write_bf16_kernel, dim3(blocks), dim3(256), stream, ev,
+                       (const uint16_t*)c.kv_new, (const uint16_t*)c.pe_new, c.start_pos,
+                       (uint16_t*)c.kv_cache, (uint16_t*)c.pe_cache, B, s, T);
 }
 
 }  // namespace mla

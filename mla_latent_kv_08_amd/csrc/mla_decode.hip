@@ -1001,22 +1001,16 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, hipStream_t s
   float* part_ml = (float*)(ws + plan.off_part_ml);
   uint16_t* olat = (uint16_t*)(ws + plan.off_olat);
   hipEvent_t* ev = (hipEvent_t*)p.trace_events;
+  auto evk = [&](int k) -> hipEvent_t const* { return ev ? ev + 2 * k : nullptr; };
   hipError_t err;
-#define MLA_TRACE(i)                                       \
-  if (ev) {                                                \
-    err = hipEventRecord(ev[i], stream);                   \
-    if (err != hipSuccess) return err;                     \
-  }
-
   int32_t* wcum = (int32_t*)(ws + plan.off_wcum);
   int32_t* wg_seq = (int32_t*)(ws + plan.off_wg_seq);
 
-  MLA_TRACE(0);
-  absorb_kernel<<<dim3(plan.heads_padded + 1, 4), 256, 0, stream>>>(
-      (const uint16_t*)d.q_nope, (const uint16_t*)d.q_pe, (const uint16_t*)d.wkv_b, qt, B, H,
-      plan.heads_padded, d.cache_lens, p.max_seq_len, p.topk, plan.min_group_tiles, wcum, wg_seq);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  MLA_TRACE(1);
+  err = launch_kernel(absorb_kernel, dim3(plan.heads_padded + 1, 4), dim3(256), stream, evk(0),
+                      (const uint16_t*)d.q_nope, (const uint16_t*)d.q_pe, (const uint16_t*)d.wkv_b,
+                      qt, B, H, plan.heads_padded, d.cache_lens, p.max_seq_len, p.topk,
+                      plan.min_group_tiles, wcum, wg_seq);
+  if (err != hipSuccess) return err;
 
   AttnArgs aa;
   aa.qt = qt;
@@ -1037,26 +1031,19 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, hipStream_t s
   aa.head_blocks = plan.head_blocks;
   aa.scale_log2 = p.softmax_scale * 1.4426950408889634f;
   const dim3 agrid((unsigned)plan.max_groups);
-  MLA_TRACE(2);
   const bool fp8 = p.kv_dtype == MLA_KV_FP8_E4M3_B128, topk = p.topk > 0;
-  if (fp8 && topk) attn_kernel<true, true><<<agrid, kAttnThreads, 0, stream>>>(aa);
-  else if (fp8) attn_kernel<true, false><<<agrid, kAttnThreads, 0, stream>>>(aa);
-  else if (topk) attn_kernel<false, true><<<agrid, kAttnThreads, 0, stream>>>(aa);
-  else attn_kernel<false, false><<<agrid, kAttnThreads, 0, stream>>>(aa);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  MLA_TRACE(3);
+  auto attn = fp8 ? (topk ? attn_kernel<true, true> : attn_kernel<true, false>)
+                  : (topk ? attn_kernel<false, true> : attn_kernel<false, false>);
+  err = launch_kernel(attn, agrid, dim3(kAttnThreads), stream, evk(1), aa);
+  if (err != hipSuccess) return err;
 
-  MLA_TRACE(4);
-  combine_kernel<<<dim3(H, B, 2), 256, 0, stream>>>(part_o, part_ml, wcum, olat, H);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  MLA_TRACE(5);
+  err = launch_kernel(combine_kernel, dim3(H, B, 2), dim3(256), stream, evk(2),
+                      (const uint16_t*)part_o, (const float*)part_ml, (const int32_t*)wcum, olat, H);
+  if (err != hipSuccess) return err;
 
-  MLA_TRACE(6);
-  uproj_kernel<<<dim3(H, 4), 64, 0, stream>>>(olat, (const uint16_t*)d.wkv_b,
-                                                           (uint16_t*)d.out, B, H);
-  if ((err = hipGetLastError()) != hipSuccess) return err;
-  MLA_TRACE(7);
-#undef MLA_TRACE
+  err = launch_kernel(uproj_kernel, dim3(H, 4), dim3(64), stream, evk(3), (const uint16_t*)olat,
+                      (const uint16_t*)d.wkv_b, (uint16_t*)d.out, B, H);
+  if (err != hipSuccess) return err;
   return hipSuccess;
 }
 

@@ -1,6 +1,7 @@
 // mla_launch.hpp -- internal interface between the C ABI (argument checks)
 // and the kernel launchers.  Arguments reaching here have been validated.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -31,6 +32,17 @@ struct CacheWriteArgs {
 };
 
 hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, hipStream_t stream);
+
+// Launch `kernel` on `stream`.  With `ev` non-null the start and end of the
+// dispatch are stamped into ev[0] and ev[1] by the dispatch itself (no extra
+// queue packets, so the elapsed time is the kernel's own duration).
+template <typename... KArgs, typename... Args>
+hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                         hipEvent_t const* ev, Args... args) {
+  if (ev) hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev[0], ev[1], 0, args...);
+  else hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+  return hipGetLastError();
+}
 hipError_t launch_cache_write(const mla_params& p, const CacheWriteArgs& c, hipStream_t stream);
 
 }  // namespace mla
