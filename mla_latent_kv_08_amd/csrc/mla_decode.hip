@@ -62,15 +62,18 @@ __device__ long long block_reduce_256(long long v, long long* red) {
   return r;
 }
 
-constexpr int kPlanCache = 4096;  // tile counts kept in LDS by the planner
+constexpr int kPlanCache = 2048;  // per-sequence values kept in LDS by the planner
 
 // Work plan of one decode call, computed by one workgroup of 256 threads (the
 // split is described with make_decode_plan): picks the tile budget S, then
-// writes wcum[b] = k_0 + ... + k_{b-1} (wcum[B] = workgroups in use) and
-// wg_seq[i] = the sequence of workgroup i.
-__device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min_tiles,
-                            int32_t* wcum, int32_t* wg_seq) {
-  __shared__ int tl[kPlanCache];
+// writes wcum[b] = k_0 + ... + k_{b-1} (wcum[B] = workgroups in use) and, for
+// each of the G attention workgroups, the record {sequence, first tile, end
+// tile, clamped length} (sequence -1: workgroup unused), so that a workgroup
+// starts from one 16-byte load.
+__device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min_tiles, int G,
+                            int32_t* wcum, int4* rec) {
+  __shared__ int tl[kPlanCache];       // tiles of sequence b
+  __shared__ int sw[kPlanCache + 1];   // first workgroup of sequence b
   __shared__ int sc[256];
   __shared__ long long red[4];
   const int tid = threadIdx.x;
@@ -78,16 +81,18 @@ __device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min
     return (selected_entries(seq_len(lens, bb, T), topk) + kTileRows - 1) / kTileRows;
   };
   auto tiles = [&](int bb) -> int { return bb < kPlanCache ? tl[bb] : tiles_of(bb); };
-  long long tot = 0, mx = 0;
+  long long tot = 0, mx = 0, nonempty = 0;
   for (int bb = tid; bb < B; bb += 256) {
     const int t = tiles_of(bb);
     if (bb < kPlanCache) tl[bb] = t;
     tot += t;
     mx = t > mx ? t : mx;
+    nonempty += t > 0;
   }
   __syncthreads();
   tot = block_reduce_256<false>(tot, red);
   mx = block_reduce_256<true>(mx, red);
+  nonempty = block_reduce_256<false>(nonempty, red);
   // workgroups needed with budget S
   auto groups_for = [&](long long S) -> long long {
     long long c = 0;
@@ -95,9 +100,14 @@ __device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min
     return block_reduce_256<false>(c, red);
   };
   long long S = mx > 0 ? mx : 1;
-  if (mx > 0 && groups_for(mx) <= kTargetCUs) {
-    long long lo = (tot + kTargetCUs - 1) / kTargetCUs, hi = mx;  // groups_for(hi) fits
+  if (mx > 0 && nonempty < kTargetCUs) {
+    // sum ceil(t_b / S) <= tot / S + nonempty, so S = ceil(tot / (256 - nonempty))
+    // fits, and nothing below ceil(tot / 256) does: search between the two
+    long long lo = (tot + kTargetCUs - 1) / kTargetCUs;
+    long long hi = (tot + (kTargetCUs - nonempty) - 1) / (kTargetCUs - nonempty);
     if (lo < 1) lo = 1;
+    if (hi > mx) hi = mx;  // S = mx gives one workgroup per sequence, which fits
+    if (lo > hi) lo = hi;
     while (lo < hi) {  // smallest S in [lo, hi] that fits (groups_for is non-increasing)
       const long long mid = (lo + hi) / 2;
       if (groups_for(mid) <= kTargetCUs) hi = mid;
@@ -114,11 +124,38 @@ __device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min
     const int incl = block_scan_256(k, sc, &total);
     if (bb < B) {
       wcum[bb + 1] = run + incl;
-      for (int i = run + incl - k; i < run + incl; ++i) wg_seq[i] = bb;
+      if (bb <= kPlanCache) sw[bb] = run + incl - k;
+      if (bb >= kPlanCache) {  // long batches: these records come from the sequence's own thread
+        const int t = tiles_of(bb), len = seq_len(lens, bb, T);
+        for (int p = 0; p < k; ++p)
+          rec[run + incl - k + p] =
+              make_int4(bb, (int)((long long)p * t / k), (int)((long long)(p + 1) * t / k), len);
+      }
     }
     run += total;
   }
-  if (tid == 0) wcum[0] = 0;
+  const int nb_cached = B < kPlanCache ? B : kPlanCache;
+  if (tid == 0) {
+    wcum[0] = 0;
+    if (B <= kPlanCache) sw[B] = run;
+  }
+  __syncthreads();
+  // records of the workgroups of the first nb_cached sequences, one per
+  // thread: workgroup i belongs to the last sequence b with sw[b] <= i
+  // (sequences without tiles share their successor's sw, so they are never
+  // the last one below a used workgroup)
+  const int used_cached = sw[nb_cached];
+  for (int i = tid; i < used_cached; i += 256) {
+    int lo = 0, hi = nb_cached - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sw[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    const int t = tl[lo], k = sw[lo + 1] - sw[lo], p = i - sw[lo];
+    rec[i] = make_int4(lo, (int)((long long)p * t / k), (int)((long long)(p + 1) * t / k), seq_len(lens, lo, T));
+  }
+  for (int i = run + tid; i < G; i += 256) rec[i] = make_int4(-1, 0, 0, 0);
 }
 
 // ---------------------------------------------------------------------------
@@ -135,10 +172,10 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
                                                      uint16_t* __restrict__ qt, int B, int H,
                                                      int Hp, const int32_t* __restrict__ lens,
                                                      int T, int topk, int min_group_tiles,
-                                                     int32_t* wcum, int32_t* wg_seq) {
+                                                     int G, int32_t* wcum, int4* rec) {
   const int h = blockIdx.x, cblk = blockIdx.y, tid = threadIdx.x;
   if (h == Hp) {
-    if (cblk == 0) plan_groups(lens, B, T, topk, min_group_tiles, wcum, wg_seq);
+    if (cblk == 0) plan_groups(lens, B, T, topk, min_group_tiles, G, wcum, rec);
     return;
   }
   const int cq = tid & 15, dq = tid >> 4;
@@ -253,10 +290,8 @@ struct AttnArgs {
   const void* kv;
   const float* kv_scale;
   const uint16_t* pe;
-  const int32_t* lens;
   const int32_t* topk_idx;
-  const int32_t* wcum;    // [B + 1] first workgroup of each sequence
-  const int32_t* wg_seq;  // [grid] sequence of each workgroup
+  const int4* rec;        // [grid] {sequence or -1, first tile, end tile, length}
   uint16_t* part_o;       // [grid][H][512]
   float* part_ml;         // [grid][H][2]
   int B, H, Hp, T, topk, head_blocks;
@@ -315,13 +350,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   const int grp = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (grp >= a.wcum[a.B]) return;  // whole workgroup: not used by the plan
-  const int b = a.wg_seq[grp];
-  const int wb = a.wcum[b], kb = a.wcum[b + 1] - wb, piece = grp - wb;
-  const int len = a.lens[b] < 0 ? 0 : (a.lens[b] > a.T ? a.T : a.lens[b]);
+  const int4 rec = a.rec[grp];
+  if (rec.x < 0) return;  // whole workgroup: not used by the plan
+  const int b = rec.x, t_lo = rec.y, t_hi = rec.z, len = rec.w;
   const int n_b = TOPK ? (len > 0 ? a.topk : 0) : len;
-  const int tb = (n_b + kTT - 1) / kTT;
-  const int t_lo = (int)((long long)piece * tb / kb), t_hi = (int)((long long)(piece + 1) * tb / kb);
   const int p0 = t_lo * kTT, p1 = min(t_hi * kTT, n_b);
   const int ntiles = t_hi - t_lo;
   const size_t seq_row0 = (size_t)b * a.T;
@@ -351,9 +383,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   const int head = wave * 32 + n;
 
   // P rows and l of heads without a score wave stay zero; their alpha stays 1.
-  // Slot 2 and P buffer 1 stand in for "tile -1" of the pipeline: zero.
   for (int i = tid; i < 2 * 128 * kPStride / 2; i += kAttnThreads) ((uint32_t*)sP)[i] = 0u;
-  for (int i = tid; i < kTileElems / 8; i += kAttnThreads) ((u32x4*)sT2)[i] = u32x4{0u, 0u, 0u, 0u};
   if (tid < 128) {
     sAlpha[tid] = 1.f;
     sAlpha[128 + tid] = 1.f;
@@ -617,27 +647,39 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   };
   // Update step (u, m): A = 2 transposing reads of tile pt (rows 16u + 4g + r
   // and 16u + 8 + 4g + r), B = P^T of head block nb (pb, 16 bytes per lane).
-  auto tr_read = [&](const uint16_t* pt, int u, int m) MLA_INLINE -> u32x4 {
+  auto tr_read_any = [&](const uint16_t* pt, int u, int m) MLA_INLINE -> u32x4 {
     const uint16_t* base = pt + 16 * u * kQK + 64 * (m >> 1);
     const u32x2 v0 = ds_read_tr16(base + tr_base[0][m & 1]);
     const u32x2 v1 = ds_read_tr16(base + tr_base[1][m & 1]);
     return u32x4{v0[0], v0[1], v1[0], v1[1]};
   };
-  auto pv_mfma = [&](const u32x4& va, const u32x4 (&pb)[4], int m) MLA_INLINE {
+  auto pv_mfma_any = [&](const u32x4& va, const u32x4 (&pb)[4], int m) MLA_INLINE {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) o[4 * m + nb] = mfma32(va, pb[nb], o[4 * m + nb]);
   };
-  auto pb_read = [&](const uint16_t* pp, u32x4 (&pb)[4], int u) MLA_INLINE {
+  auto pb_read_any = [&](const uint16_t* pp, u32x4 (&pb)[4], int u) MLA_INLINE {
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) pb[nb] = *(const u32x4*)(pp + (32 * nb + n) * kPStride + 16 * u + 8 * g);
   };
   // Update with tile jp interleaved with the softmax of tile j held in s:
   // eight scheduling regions, each with the four MFMAs of one update step
   // (whose A operand was read one region earlier) and a slice of the softmax.
-  auto update_softmax = [&](const uint16_t* ptile, int jp, f32x16& s, int j, uint32_t mask) MLA_INLINE {
+  auto update_softmax = [&](auto PV, const uint16_t* ptile, int jp, f32x16& s, int j,
+                            uint32_t mask) MLA_INLINE {
+    constexpr bool pv = decltype(PV)::value;  // false: softmax only (the first tile)
     const uint16_t* pp = pbuf(jp);
     u32x4 pb[4], va[3];
     float mx, m_use, m_sub, alpha;
+    auto tr_read = [&](const uint16_t* pt, int u, int m) MLA_INLINE -> u32x4 {
+      if constexpr (pv) return tr_read_any(pt, u, m);
+      else return u32x4{0u, 0u, 0u, 0u};
+    };
+    auto pv_mfma = [&](const u32x4& va, const u32x4(&pb)[4], int m) MLA_INLINE {
+      if constexpr (pv) pv_mfma_any(va, pb, m);
+    };
+    auto pb_read = [&](const uint16_t* pp, u32x4(&pb)[4], int u) MLA_INLINE {
+      if constexpr (pv) pb_read_any(pp, pb, u);
+    };
     pb_read(pp, pb, 0);
     va[0] = tr_read(ptile, 0, 0);
     va[1] = tr_read(ptile, 0, 1);
@@ -724,14 +766,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     u32x4 pb[4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      pb_read(pp, pb, u);
+      pb_read_any(pp, pb, u);
 #pragma unroll
-      for (int m = 0; m < 4; ++m) pv_mfma(tr_read(ptile, u, m), pb, m);
+      for (int m = 0; m < 4; ++m) pv_mfma_any(tr_read_any(ptile, u, m), pb, m);
     }
   };
 
   // Tile j lives in ring slot S = j % kStages (a compile-time constant here).
-  auto body = [&](int j, auto S) MLA_INLINE {
+  auto body = [&](int j, auto S, auto PV) MLA_INLINE {
     constexpr int st = decltype(S)::value;
     constexpr int s1 = (st + 1) % kStages;  // slot of tile j + 1 (held tile j - 2)
     constexpr int sp = (st + 2) % kStages;  // slot of tile j - 1
@@ -797,17 +839,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
       full_all(ft);
     }
     const uint32_t mask = sMask[st];
-    // one code path for every wave and tile (branches around the update would
-    // merge 256 accumulator registers): for j = 0 the update runs on the
-    // zeroed slot and P buffer of "tile -1"
-    rescale(j - 1);
-    update_softmax(slot(Stage<sp>{}), j - 1, s, j, mask);
+    // one code path for every wave inside the loop (branches around the
+    // update would merge 256 accumulator registers); the first tile, which
+    // has no update before it, is peeled off the loop
+    if constexpr (decltype(PV)::value) rescale(j - 1);
+    update_softmax(PV, slot(Stage<sp>{}), j - 1, s, j, mask);
     if (FP8 && j + 1 < ntiles) store_fp8(j + 1, Stage<s1>{});
   };
-  for (int j0 = 0; j0 < ntiles; j0 += kStages) {
-    body(j0, Stage<0>{});
-    if (j0 + 1 < ntiles) body(j0 + 1, Stage<1>{});
-    if (j0 + 2 < ntiles) body(j0 + 2, Stage<2>{});
+  body(0, Stage<0>{}, Stage<0>{});
+  for (int j0 = 1; j0 < ntiles; j0 += kStages) {
+    body(j0, Stage<1>{}, Stage<1>{});
+    if (j0 + 1 < ntiles) body(j0 + 1, Stage<2>{}, Stage<1>{});
+    if (j0 + 2 < ntiles) body(j0 + 2, Stage<0>{}, Stage<1>{});
   }
   // drain: the update with the last tile
   {
@@ -844,7 +887,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *(u32x2*)(row + 32 * m + 8 * q) =
-            u32x2{pack_bf(ob[4 * q] * inv, ob[4 * q + 1] * inv), pack_bf(ob[4 * q + 2] * inv, ob[4 * q + 3] * inv)};
+            u32x2{cvt_pk_bf16(ob[4 * q] * inv, ob[4 * q + 1] * inv), cvt_pk_bf16(ob[4 * q + 2] * inv, ob[4 * q + 3] * inv)};
     }
   };
   stage_out(Stage<0>{}, Stage<0>{});
@@ -1004,12 +1047,12 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, hipStream_t s
   auto evk = [&](int k) -> hipEvent_t const* { return ev ? ev + 2 * k : nullptr; };
   hipError_t err;
   int32_t* wcum = (int32_t*)(ws + plan.off_wcum);
-  int32_t* wg_seq = (int32_t*)(ws + plan.off_wg_seq);
+  int4* rec = (int4*)(ws + plan.off_rec);
 
   err = launch_kernel(absorb_kernel, dim3(plan.heads_padded + 1, 4), dim3(256), stream, evk(0),
                       (const uint16_t*)d.q_nope, (const uint16_t*)d.q_pe, (const uint16_t*)d.wkv_b,
                       qt, B, H, plan.heads_padded, d.cache_lens, p.max_seq_len, p.topk,
-                      plan.min_group_tiles, wcum, wg_seq);
+                      plan.min_group_tiles, (int)plan.max_groups, wcum, rec);
   if (err != hipSuccess) return err;
 
   AttnArgs aa;
@@ -1017,10 +1060,8 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, hipStream_t s
   aa.kv = d.kv_cache;
   aa.kv_scale = d.kv_scale;
   aa.pe = (const uint16_t*)d.pe_cache;
-  aa.lens = d.cache_lens;
   aa.topk_idx = d.topk_idx;
-  aa.wcum = wcum;
-  aa.wg_seq = wg_seq;
+  aa.rec = rec;
   aa.part_o = part_o;
   aa.part_ml = part_ml;
   aa.B = B;

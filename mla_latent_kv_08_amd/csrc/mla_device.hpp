@@ -41,7 +41,8 @@ __device__ __forceinline__ uint32_t pack_bf_finite(float lo, float hi) {
   return f2bf_finite(lo) | (f2bf_finite(hi) << 16);
 }
 // Two fp32 -> packed bf16 with gfx950's v_cvt_pk_bf16_f32 (round to nearest
-// even); used for values that stay inside the kernel (softmax probabilities).
+// even, NaN stays NaN); used for the softmax probabilities and the normalised
+// partial outputs of the attention kernel.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {

@@ -21,7 +21,9 @@ constexpr int kMaxTopkGroupTiles = 32;  // top-k: tiles per workgroup (index sta
 // workgroups, and workgroup i = w_b + p (w_b = k_0 + ... + k_{b-1}) takes its
 // tiles [floor(p t_b / k_b), floor((p+1) t_b / k_b)) and writes its partial
 // (O, m, l) into slot i.  S is the smallest budget with sum k_b <= 256 (one
-// round), at least min_group_tiles, and at most 32 with a top-k selection.
+// round), at least min_group_tiles (2: a workgroup's fixed costs, the query
+// load and the 128 KB partial, then cover at least two tiles), and at most 32
+// with a top-k selection.
 // The lengths live on the device, so w_b and S are computed there; the sizes
 // here are upper bounds.
 struct DecodePlan {
@@ -30,7 +32,7 @@ struct DecodePlan {
   long long max_groups; // attention grid (upper bound of sum k_b)
   int min_group_tiles;  // lower bound of S
   long long max_tiles;  // tiles of the longest possible selection
-  size_t off_qt, off_part_o, off_part_ml, off_olat, off_wcum, off_wg_seq, bytes;
+  size_t off_qt, off_part_o, off_part_ml, off_olat, off_wcum, off_rec, bytes;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -42,7 +44,7 @@ inline DecodePlan make_decode_plan(const mla_params& p) {
   d.head_blocks = d.heads_padded / 32;
   const long long n_max = p.topk > 0 ? p.topk : p.max_seq_len;
   d.max_tiles = (n_max + kTileRows - 1) / kTileRows;
-  d.min_group_tiles = 1;
+  d.min_group_tiles = 2;
   long long G = B > kTargetCUs ? B : kTargetCUs;
   if (p.topk > 0) {
     const long long capped = (long long)B * ((d.max_tiles + kMaxTopkGroupTiles - 1) / kMaxTopkGroupTiles);
@@ -60,8 +62,8 @@ inline DecodePlan make_decode_plan(const mla_params& p) {
   off = align256(off + (size_t)B * H * 512 * 2);
   d.off_wcum = off;  // int32 [B + 1]: w_b, w_B = workgroups in use
   off = align256(off + ((size_t)B + 1) * 4);
-  d.off_wg_seq = off;  // int32 [max_groups]
-  off = align256(off + (size_t)G * 4);
+  d.off_rec = off;  // int32 [max_groups][4]: sequence (-1: unused), first tile, end tile, length
+  off = align256(off + (size_t)G * 16);
   d.bytes = off;
   return d;
 }

@@ -113,6 +113,18 @@ def test_ragged_small_with_poison(m):
     assert (out[0].float() == 0).all()  # length 0 -> zeros
 
 
+def test_many_sequences(m):
+    # more sequences than the work planner keeps in LDS (2048): the rest of the
+    # plan takes the per-sequence path; lengths include empty and full ones
+    w = synth.Workload("many", 2100, 16, 70, ragged=(0, 70), seed=11)
+    x = synth.make_inputs(w)
+    lens = x["cache_lens"].clone()
+    lens[::7] = 0
+    lens[3::11] = 70
+    x["cache_lens"] = lens
+    run_case(m, w, x, label="B2100")
+
+
 def test_topk_small(m):
     w = synth.Workload("topk", 3, 128, 2000, topk=300, seed=6)
     x = synth.make_inputs(w)
