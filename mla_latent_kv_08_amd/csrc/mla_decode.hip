@@ -283,6 +283,8 @@ constexpr int kAttnWaves = 4;
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kPStride = 40;                // bf16 per sP row (32 + 8 padding)
 constexpr int kOStride = 520;               // bf16 per staged output row (512 + 8 padding)
+constexpr int kFp8Codes = kTT * kC;                       // bytes of latent codes per tile
+constexpr int kFp8Stage = kFp8Codes + kTT * 16 + kTT * kR * 2;  // + scales + rotary rows
 static_assert(32 * kOStride <= kTileElems, "a 32-head block of O fits one ring slot");
 
 struct AttnArgs {
@@ -370,6 +372,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   __shared__ uint32_t sMask[kStages];
   __shared__ uint32_t sRescale[3];  // by tile mod 3: some head of the tile rescales
   __shared__ int sIdx[TOPK ? kMaxIdx : 1];
+  // FP8 cache: raw tile (codes [32][512] B, scales [32][4] fp32, rotary
+  // [32][64] bf16) staged by direct loads one tile ahead
+  __shared__ __attribute__((aligned(16))) uint8_t sF[FP8 ? kFp8Stage : 16];
   static_assert(kStages == 3, "one LDS array per ring slot");
   auto slot = [&](auto S) MLA_INLINE -> uint16_t* {
     constexpr int st = decltype(S)::value;
@@ -560,40 +565,62 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     full_load(ft, Stage<8>{});
   };
 
-  // ---- FP8 tiles through registers: 4 units of 16 codes + 1 rotary chunk per thread
-  u32x4 c8[FP8 ? 4 : 1];
-  float csc[FP8 ? 4 : 1];
-  u32x4 pev;
-  auto load_fp8 = [&](int j) MLA_INLINE {
+  // ---- FP8 tiles: the raw tile is copied global -> LDS (sF) one tile ahead:
+  // 16 loads of 1 KB for the codes (two rows each), 4 for the rotary rows
+  // (eight rows each) and one of 512 B for the scales; wave w issues loads
+  // w, w+4, ... (wave 0 also the scales).  The dequantisation pass then turns
+  // sF into the bf16 tile in its ring slot, 16 codes per thread and unit.
+  auto issue_fp8 = [&](int j) MLA_INLINE {
     const int pt = p0 + j * kTT;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int u = tid + kAttnThreads * k, t = u >> 5, cc = u & 31;
-      const size_t row = seq_row0 + tile_row(pt, t);
-      c8[k] = *(const u32x4*)((const uint8_t*)a.kv + row * kC + cc * 16);
-      csc[k] = a.kv_scale[row * 4 + (cc >> 3)];
+    uint32_t base = lds_addr(sF);
+    asm volatile("" : "+s"(base));
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // recomputed per tile
+    auto one = [&](auto I) MLA_INLINE {
+      constexpr int i = decltype(I)::value;  // load i = wave + 4k, k < 5 (i < 20)
+      const int li = wave + 4 * i;
+      if (li < 16) {  // codes of rows 2 li + (lane >> 5)
+        const size_t row = seq_row0 + tile_row(pt, 2 * li + (ln >> 5));
+        lds_dma16<0>((const uint8_t*)a.kv + row * kC + (ln & 31) * 16, base + 1024 * li);
+      } else {  // rotary rows 8 (li - 16) + (lane >> 3)
+        const size_t row = seq_row0 + tile_row(pt, 8 * (li - 16) + (ln >> 3));
+        lds_dma16<kFp8Codes + kTT * 16>(a.pe + row * kR + (ln & 7) * 8, base + 1024 * (li - 16));
+      }
+    };
+    one(Stage<0>{});
+    one(Stage<1>{});
+    one(Stage<2>{});
+    one(Stage<3>{});
+    one(Stage<4>{});
+    if (wave == 0 && ln < 32) {  // scales of row `lane`
+      const size_t row = seq_row0 + tile_row(pt, ln);
+      lds_dma16<kFp8Codes>(a.kv_scale + row * 4, base);
     }
-    const size_t row = seq_row0 + tile_row(pt, tid >> 3);
-    pev = *(const u32x4*)(a.pe + row * kR + (tid & 7) * 8);
   };
-  auto store_fp8 = [&](int j, auto S) MLA_INLINE {
-    const int stage = decltype(S)::value;
+  auto dequant_fp8 = [&](int j, auto S) MLA_INLINE {
     uint16_t* dst = slot(S);
+    const float* scl = (const float*)(sF + kFp8Codes);
+    int th = tid;
+    asm volatile("" : "+v"(th));  // addresses recomputed per tile, not kept live per slot
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const int u = tid + kAttnThreads * k, t = u >> 5, cc = u & 31;
+      const int u = th + kAttnThreads * k, t = u >> 5, cc = u & 31;
+      const u32x4 q = *(const u32x4*)(sF + t * kC + cc * 16);
+      const float sc = scl[t * 4 + (cc >> 3)];
       uint32_t w[8];
 #pragma unroll
       for (int d = 0; d < 4; ++d) {
-        const uint32_t q = c8[k][d];
-        w[2 * d] = pack_bf(e4m3fn_to_f32(q & 0xFFu) * csc[k], e4m3fn_to_f32((q >> 8) & 0xFFu) * csc[k]);
-        w[2 * d + 1] = pack_bf(e4m3fn_to_f32((q >> 16) & 0xFFu) * csc[k], e4m3fn_to_f32(q >> 24) * csc[k]);
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[d], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[d], true);
+        w[2 * d] = cvt_pk_bf16(lo[0] * sc, lo[1] * sc);
+        w[2 * d + 1] = cvt_pk_bf16(hi[0] * sc, hi[1] * sc);
       }
       *(u32x4*)(dst + tile_off(t, 2 * cc)) = u32x4{w[0], w[1], w[2], w[3]};
       *(u32x4*)(dst + tile_off(t, 2 * cc + 1)) = u32x4{w[4], w[5], w[6], w[7]};
     }
-    *(u32x4*)(dst + tile_off(tid >> 3, 64 + (tid & 7))) = pev;
-    publish_mask(p0 + j * kTT, stage);
+    const u32x4 pv = *(const u32x4*)(sF + kFp8Codes + kTT * 16 + th * 16);
+    *(u32x4*)(dst + tile_off(th >> 3, 64 + (th & 7))) = pv;
+    publish_mask(p0 + j * kTT, decltype(S)::value);
   };
 
   // O accumulators o[4 * m + nb]: columns 128w + 32m + ..., heads 32nb + ...
@@ -610,7 +637,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   // ---- pipeline prologue: the first tiles and the query are loaded
   // together, and everything is complete before the loop
   if (!FP8) issue_bf16(0, Stage<0>{});
-  else load_fp8(0);
+  else issue_fp8(0);
   // Absorbed query + q_pe of this lane's head: k-step s covers elements
   // 16s..16s+15, lane group g holds 8 of them.
   u32x4 qreg[36];
@@ -620,7 +647,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     for (int st = 0; st < 36; ++st) qreg[st] = src[2 * st + g];
   }
   MLA_WAIT_VMCNT(0);
-  if (FP8) store_fp8(0, Stage<0>{});
+  if (FP8) {  // tile 0 into slot 0, then the raw tile 1 on its way
+    MLA_LDS_BARRIER();
+    dequant_fp8(0, Stage<0>{});
+    MLA_LDS_BARRIER();
+    if (1 < ntiles) issue_fp8(1);
+  }
 
   // ---- software pipeline over the tiles, one workgroup barrier per tile.
   // Body j: barrier; loads of tile j+1 (slot of tile j-2); scores of tile j;
@@ -781,16 +813,24 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     // own loads of it); P, alpha and flag of tile j-1 visible; every wave is
     // done with tile j-2 and with the P buffer and flag the softmax of tile j
     // is about to write.
-    if (!FP8) MLA_WAIT_VMCNT(0);
+    MLA_WAIT_VMCNT(0);
     MLA_LDS_BARRIER();
     // tile j+1: a full dense tile is loaded by the fast path, its nine loads
-    // per thread spread over the score MFMAs; any other tile in one burst here
+    // per thread spread over the score MFMAs; any other tile in one burst here.
+    // FP8: the raw tile j+1 (staged during tile j-1) is dequantised into its
+    // slot, then a second barrier frees the staging buffer for tile j+2.
     const bool fast = !FP8 && !TOPK && j + 1 < ntiles && p0 + (j + 2) * kTT <= p1;
     const FullTile ft = full_tile(j + 1, Stage<s1>{});
     if (j + 1 < ntiles) {
-      if (FP8) load_fp8(j + 1);
-      else if (fast) publish_mask(p0 + (j + 1) * kTT, s1);
-      else issue_bf16(j + 1, Stage<s1>{});
+      if (FP8) {
+        dequant_fp8(j + 1, Stage<s1>{});
+        MLA_LDS_BARRIER();
+        if (j + 2 < ntiles) issue_fp8(j + 2);
+      } else if (fast) {
+        publish_mask(p0 + (j + 1) * kTT, s1);
+      } else {
+        issue_bf16(j + 1, Stage<s1>{});
+      }
     }
     if (tid == 0) sRescale[(j + 1) % 3] = 0u;  // flag of tile j-2: read in body j-1
     const uint16_t* tile = slot(S);
@@ -844,7 +884,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     // has no update before it, is peeled off the loop
     if constexpr (decltype(PV)::value) rescale(j - 1);
     update_softmax(PV, slot(Stage<sp>{}), j - 1, s, j, mask);
-    if (FP8 && j + 1 < ntiles) store_fp8(j + 1, Stage<s1>{});
   };
   body(0, Stage<0>{}, Stage<0>{});
   for (int j0 = 1; j0 < ntiles; j0 += kStages) {
