@@ -282,6 +282,7 @@ constexpr int kMaxIdx = kMaxTopkGroupTiles * kTT;  // top-k entries staged per w
 constexpr int kAttnWaves = 4;
 constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kPStride = 40;                // bf16 per sP row (32 + 8 padding)
+constexpr int kScoreAhead = 4;              // score operand reads issued ahead of their MFMA
 constexpr int kOStride = 520;               // bf16 per staged output row (512 + 8 padding)
 constexpr int kFp8Codes = kTT * kC;                       // bytes of latent codes per tile
 constexpr int kFp8Stage = kFp8Codes + kTT * 16 + kTT * kR * 2;  // + scales + rotary rows
@@ -699,8 +700,22 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   auto update_softmax = [&](auto PV, const uint16_t* ptile, int jp, f32x16& s, int j,
                             uint32_t mask) MLA_INLINE {
     constexpr bool pv = decltype(PV)::value;  // false: softmax only (the first tile)
+    // In-order issue: VALU work only runs under an MFMA if it sits between
+    // MFMAs in program order, so each region is laid out as its LDS reads,
+    // then MFMA, VALU x5, MFMA, VALU x5, ... (masks: 0x100 LDS read, 0x8
+    // MFMA, 0x2 VALU, 0x200 LDS write).
+    auto interleave = [&]() MLA_INLINE {
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x002, 64, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
+    };
     const uint16_t* pp = pbuf(jp);
-    u32x4 pb[4], va[3];
+    u32x4 pb[4], va[4];
     float mx, m_use, m_sub, alpha;
     auto tr_read = [&](const uint16_t* pt, int u, int m) MLA_INLINE -> u32x4 {
       if constexpr (pv) return tr_read_any(pt, u, m);
@@ -715,8 +730,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     pb_read(pp, pb, 0);
     va[0] = tr_read(ptile, 0, 0);
     va[1] = tr_read(ptile, 0, 1);
-    // region 0 (A operands are read two steps ahead of their MFMAs)
     va[2] = tr_read(ptile, 0, 2);
+    // region 0 (A operands are read three steps ahead of their MFMAs)
+    va[3] = tr_read(ptile, 0, 3);
     pv_mfma(va[0], pb, 0);
     if (mask != 0xFFFFFFFFu) {  // partial tile (wave-uniform branch)
       const uint32_t ml = (mask >> (4 * g)) & 0x0F0F0F0Fu;  // rows 8a + 4g + b -> bit 8a + b
@@ -725,9 +741,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
         if (!((ml >> (8 * (e >> 2) + (e & 3))) & 1u)) s[e] = -INFINITY;
     }
     mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
     // region 1: the other 16 rows of this lane's head sit in lane l ^ 32
-    va[0] = tr_read(ptile, 0, 3);
+    va[0] = tr_read(ptile, 1, 0);
     pv_mfma(va[1], pb, 1);
     mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(s[8], s[9]), fmaxf(s[10], s[11])),
                          fmaxf(fmaxf(s[12], s[13]), fmaxf(s[14], s[15]))));
@@ -735,11 +752,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
     // region 2: online softmax in log2 units; the running max only moves when
     // the new one exceeds it by more than 8 (probabilities stay <= 2^8), which
     // skips most rescales of O without changing the result
-    va[1] = tr_read(ptile, 1, 0);
+    va[1] = tr_read(ptile, 1, 1);
     pv_mfma(va[2], pb, 2);
     {
       const float mt = mx * a.scale_log2;
@@ -749,31 +767,34 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], a.scale_log2, -m_sub));
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
-    // region 3 (then the B operand of the second k-step)
-    va[2] = tr_read(ptile, 1, 1);
-    pv_mfma(va[0], pb, 3);
+    // region 3
+    va[2] = tr_read(ptile, 1, 2);
+    pv_mfma(va[3], pb, 3);
+    pb_read(pp, pb, 1);  // B operand of the second k-step
 #pragma unroll
     for (int e = 4; e < 8; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], a.scale_log2, -m_sub));
-    pb_read(pp, pb, 1);
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
     // region 4
-    va[0] = tr_read(ptile, 1, 2);
-    pv_mfma(va[1], pb, 0);
+    va[3] = tr_read(ptile, 1, 3);
+    pv_mfma(va[0], pb, 0);
 #pragma unroll
     for (int e = 8; e < 12; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], a.scale_log2, -m_sub));
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
     // region 5
-    va[1] = tr_read(ptile, 1, 3);
-    pv_mfma(va[2], pb, 1);
+    pv_mfma(va[1], pb, 1);
 #pragma unroll
     for (int e = 12; e < 16; ++e) s[e] = __builtin_amdgcn_exp2f(fmaf(s[e], a.scale_log2, -m_sub));
     const float lsum = (((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]))) +
                        (((s[8] + s[9]) + (s[10] + s[11])) + ((s[12] + s[13]) + (s[14] + s[15])));
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
     // region 6: P rows 8a + 4g + b land at tau = 16(a>>1) + 8g + 4(a&1) + b:
     // two contiguous 16-byte pieces per lane
-    pv_mfma(va[0], pb, 2);
+    pv_mfma(va[2], pb, 2);
     l_run = l_run * alpha + lsum;
     m_run = m_use;
     if (active) {  // waves without score heads leave their (zero) P rows alone
@@ -783,13 +804,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
       *(u32x4*)(prow + 16) = u32x4{cvt_pk_bf16(s[8], s[9]), cvt_pk_bf16(s[10], s[11]),
                                    cvt_pk_bf16(s[12], s[13]), cvt_pk_bf16(s[14], s[15])};
     }
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
     // region 7
-    pv_mfma(va[1], pb, 3);
+    pv_mfma(va[3], pb, 3);
     if (active) {
       if (g == 0) sAlpha[(j & 1) * 128 + head] = alpha;
       if (alpha != 1.f) sRescale[j % 3] = 1u;  // benign race: every writer stores 1
     }
+    interleave();
     __builtin_amdgcn_sched_barrier(0);
   };
   // The update alone (after the last tile).
@@ -841,20 +864,23 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
       // Back-to-back MFMAs of one shape accumulating into the same registers
       // need no wait states; the s_nop after the chain covers the MFMA-write
       // -> VALU-read hazard (>= 18 wait states for this 8-pass instruction).
-      // Operand reads run four k-steps ahead of the MFMAs.
-      u32x4 ka[5];
+      // Operand reads run kScoreAhead k-steps ahead of the MFMAs (enough LDS
+      // requests in flight to cover its latency with one wave per SIMD).
+      u32x4 ka[kScoreAhead + 1];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) ka[k] = *(const u32x4*)(tile + sc_base[k & 3] + 64 * (k >> 2));
+      for (int k = 0; k < kScoreAhead; ++k) ka[k] = *(const u32x4*)(tile + sc_base[k & 3] + 64 * (k >> 2));
       // nine explicitly instantiated groups of four k-steps (keeps the chain
       // fully unrolled, so qreg is indexed by constants)
       auto step = [&](auto Q, auto KK) MLA_INLINE {
         constexpr int kk = decltype(KK)::value;
         constexpr int k = 4 * decltype(Q)::value + kk;
-        if constexpr (k + 4 < 36) ka[(k + 4) % 5] = *(const u32x4*)(tile + sc_base[(k + 4) & 3] + 64 * ((k + 4) >> 2));
+        if constexpr (k + kScoreAhead < 36)
+          ka[(k + kScoreAhead) % (kScoreAhead + 1)] =
+              *(const u32x4*)(tile + sc_base[(k + kScoreAhead) & 3] + 64 * ((k + kScoreAhead) >> 2));
         if constexpr (k == 0)
           asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(s) : "v"(ka[0]), "v"(qreg[0]));
         else
-          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(ka[k % 5]), "v"(qreg[k]));
+          asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(ka[k % (kScoreAhead + 1)]), "v"(qreg[k]));
         if constexpr (kk == 1) {
           if (fast) full_load(ft, Q);
         }
