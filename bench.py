@@ -1,9 +1,10 @@
 #!/usr/bin/env python3
 """Decode-step benchmark of the weight-absorbed MLA path on one MI355X.
 
-A step is one pass of the whole hot path over one batch: mla_cache_write of
-the new row of every sequence (position cache_lens - 1) followed by
-mla_decode over rows 0 .. cache_lens - 1 (dense, ragged or top-k).  Inputs are
+A step is one pass of the whole hot path over one batch: the fused
+mla_decode_step, which stores the new row of every sequence (position
+cache_lens - 1) and then attends over rows 0 .. cache_lens - 1 (dense, ragged
+or top-k); with --unfused, mla_cache_write followed by mla_decode.  Inputs are
 seeded synthetic tensors with the workload's shapes; they are resident in
 HBM before timing starts.  R replicas of every input rotate from step to step
 so that the working set exceeds the 256 MB Infinity Cache (consecutive layers
@@ -35,7 +36,8 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20
 METRIC = "MLA decode tokens/s + latent-cache HBM GB/s (% of peak), H=128, T=4K–64K"
-KERNELS = ["cache_write", "absorb", "attention", "combine", "uproj"]
+KERNELS = ["absorb", "attention", "combine", "uproj"]
+FUSED = True  # --unfused: the row store runs as its own mla_cache_write kernel
 
 
 class HipEvents:
@@ -103,7 +105,9 @@ def kernel_symbol(name, w):
         return "mla::attn_kernel<%s, %s>" % ("true" if w.fp8 else "false", "true" if w.topk else "false")
     if name == "cache_write":
         return "mla::cache_write_fp8_kernel" if w.fp8 else "mla::cache_write_bf16_kernel"
-    return {"absorb": "mla::absorb_kernel", "combine": "mla::combine_kernel",
+    if name == "absorb":  # template argument: 0 no row store, 1 bf16 rows, 2 FP8 rows
+        return "mla::absorb_kernel<%d>" % ((2 if w.fp8 else 1) if FUSED else 0)
+    return {"combine": "mla::combine_kernel",
             "uproj": "mla::uproj_kernel"}[name]
 
 
@@ -122,6 +126,8 @@ def workload_bytes_flops(w, lens, k):
         "uproj": (proj_w + 2 * B * H * 128, 2 * B * H * 128 * 512),
         "cache_write": (B * 2 * 576 + B * row_bytes + 4 * B, 0),
     }
+    if FUSED:  # the row stores run inside the absorb launch
+        out["absorb"] = (out["absorb"][0] + out.pop("cache_write")[0], out["absorb"][1])
     total_bytes = (2 * B * H * 192 + 2 * proj_w + n_rows * row_bytes + 4 * B + 4 * B * k
                    + 2 * B * H * 128)
     total_flops = 4 * B * H * 128 * 512 + n_rows * H * 2 * (576 + 512)
@@ -160,6 +166,11 @@ def build_replicas(w, x, R, mla, torch):
 
 
 def step(mla, r, s, out, ws, trace=None):
+    if FUSED:
+        mla.decode_step(r["kv_new"], r["pe_new"], r["q_nope"], r["q_pe"], r["wkv_b"], r["kv"],
+                        r["pe"], s["lens"], kv_scale=r["scale"], topk_idx=s["topk"], out=out,
+                        workspace=ws, trace_events=None if trace is None else trace[1])
+        return
     mla.cache_write(r["kv_new"], r["pe_new"], s["start"], r["kv"], r["pe"], kv_scale=r["scale"],
                     trace_events=None if trace is None else trace[0])
     mla.decode(r["q_nope"], r["q_pe"], r["wkv_b"], r["kv"], r["pe"], s["lens"], kv_scale=r["scale"],
@@ -205,10 +216,14 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches, not graph replay")
+    ap.add_argument("--unfused", action="store_true",
+                    help="mla_cache_write then mla_decode instead of mla_decode_step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 5 plain device copies of BYTES bytes (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
+    global FUSED
+    FUSED = not args.unfused
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the decode path runs on one GPU; see the sharding notes)", file=sys.stderr)
@@ -289,11 +304,12 @@ def main():
         step(mla, reps[i % R], shared, out, ws,
              trace=(ctypes.addressof(traces[i][0]), ctypes.addressof(traces[i][1])))
     torch.cuda.synchronize()
-    dur = {kname: [] for kname in KERNELS}
+    dur = {kname: [] for kname in ([] if FUSED else ["cache_write"]) + KERNELS}
     for i in range(args.steps):
         e = ev[10 * i: 10 * i + 10]
-        dur["cache_write"].append(hev.elapsed_ms(e[0], e[1]))
-        for j, kname in enumerate(KERNELS[1:]):
+        if not FUSED:
+            dur["cache_write"].append(hev.elapsed_ms(e[0], e[1]))
+        for j, kname in enumerate(KERNELS):
             dur[kname].append(hev.elapsed_ms(e[2 + 2 * j], e[3 + 2 * j]))
     hev.destroy(ev)
     avg_us = {kname: 1e3 * float(np.mean(v)) for kname, v in dur.items()}
@@ -333,6 +349,7 @@ def main():
             "selection": (f"top-{k}" if k else ("ragged U{%d..%d}" % w.ragged if w.ragged else "dense")),
             "rows_per_step": n_rows, "replicas": R,
             "launch": "eager" if args.eager else "hip graph replay",
+            "entry": "mla_decode_step" if FUSED else "mla_cache_write + mla_decode",
         },
         "latent_cache_gbps": latent_bytes / step_s / 1e9,
         "step_hbm_gbps": total_bytes / step_s / 1e9,

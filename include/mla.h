@@ -161,6 +161,33 @@ mla_status mla_decode(const mla_params* p, const void* q_nope, const void* q_pe,
                       const void* pe_cache, const int32_t* cache_lens, const int32_t* topk_idx,
                       void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * mla_decode_step -- the fused decode step: store each sequence's new latent
+ * and rotary row, then attend with it included.
+ *
+ * A decoding token's own compressed row joins the cache before its query
+ * attends ("DeepSeek-V3.2-Exp . KV cache", the cache-write and "MQA decode"
+ * excerpts; MLA article section 3, the cached latent per token).  The result
+ * equals mla_cache_write with s = 1 and start_pos[b] = cache_lens[b] - 1,
+ * followed by mla_decode with the same arguments, but needs no extra launch:
+ * the row stores run in spare workgroups of the absorb kernel.
+ *
+ *   kv_new     bf16 [B][1][512]: new latent row c_KV of each sequence
+ *   pe_new     bf16 [B][1][64]:  new rotary row k_R (already rotated)
+ *   kv_cache, kv_scale, pe_cache: as for mla_cache_write, written at row
+ *              cache_lens[b] - 1 of sequence b (nothing is written where that
+ *              row is outside [0, T)), then read as for mla_decode
+ *   every other argument, the workspace size and the trace events: as for
+ *   mla_decode (the row stores are part of kernel 0's time)
+ * Checks, errors and a rejected call enqueue nothing, as for mla_decode.  Two
+ * sequences must not share cache rows.
+ */
+mla_status mla_decode_step(const mla_params* p, const void* kv_new, const void* pe_new,
+                           const void* q_nope, const void* q_pe, const void* wkv_b,
+                           void* kv_cache, float* kv_scale, void* pe_cache,
+                           const int32_t* cache_lens, const int32_t* topk_idx, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* mla_status_string(mla_status s);
 

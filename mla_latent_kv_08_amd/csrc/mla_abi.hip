@@ -106,10 +106,16 @@ mla_status mla_decode_workspace_size(const mla_params* p, size_t* bytes) {
   return ok();
 }
 
-mla_status mla_decode(const mla_params* p, const void* q_nope, const void* q_pe,
-                      const void* wkv_b, const void* kv_cache, const float* kv_scale,
-                      const void* pe_cache, const int32_t* cache_lens, const int32_t* topk_idx,
-                      void* out, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks of mla_decode's arguments (also those of the fused step); on success
+// *plan holds the split of the call.  MLA_OK with batch == 0 means no-op.
+mla_status check_decode(const mla_params* p, const void* q_nope, const void* q_pe,
+                        const void* wkv_b, const void* kv_cache, const float* kv_scale,
+                        const void* pe_cache, const int32_t* cache_lens, const int32_t* topk_idx,
+                        void* out, void* workspace, size_t workspace_bytes, mla::DecodePlan* plan) {
   mla_status st = check_params(p);
   if (st != MLA_OK) return st;
   if (p->seqlen_q != 1)
@@ -121,7 +127,7 @@ mla_status mla_decode(const mla_params* p, const void* q_nope, const void* q_pe,
   if (!(p->softmax_scale > 0.0f) || !isfinite(p->softmax_scale))
     return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
   if (p->batch > 65535) return fail(MLA_ERR_UNSUPPORTED, "batch > 65535");
-  if (p->batch == 0) return ok();
+  if (p->batch == 0) return MLA_OK;
   const bool fp8 = p->kv_dtype == MLA_KV_FP8_E4M3_B128;
   if (!q_nope || !q_pe || !wkv_b || !kv_cache || !pe_cache || !cache_lens || !out)
     return fail(MLA_ERR_INVALID_ARG, "a required tensor pointer is NULL");
@@ -134,15 +140,49 @@ mla_status mla_decode(const mla_params* p, const void* q_nope, const void* q_pe,
     return fail(MLA_ERR_INVALID_ARG, "bf16/uint8 tensors must be 16-byte aligned");
   if (!aligned(cache_lens, 4) || (kv_scale && !aligned(kv_scale, 4)) || (topk_idx && !aligned(topk_idx, 4)))
     return fail(MLA_ERR_INVALID_ARG, "int32/fp32 tensors must be 4-byte aligned");
-  const mla::DecodePlan plan = mla::make_decode_plan(*p);
-  if (plan.max_groups > 0x7FFFFFFFLL || plan.max_groups * p->num_heads > (1LL << 40))
+  *plan = mla::make_decode_plan(*p);
+  if (plan->max_groups > 0x7FFFFFFFLL || plan->max_groups * p->num_heads > (1LL << 40))
     return fail(MLA_ERR_UNSUPPORTED, "too many attention workgroups for this batch and top-k");
-  if (!workspace || workspace_bytes < plan.bytes)
-    return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", plan.bytes,
+  if (!workspace || workspace_bytes < plan->bytes)
+    return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", plan->bytes,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 16)) return fail(MLA_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_decode(const mla_params* p, const void* q_nope, const void* q_pe,
+                      const void* wkv_b, const void* kv_cache, const float* kv_scale,
+                      const void* pe_cache, const int32_t* cache_lens, const int32_t* topk_idx,
+                      void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  mla::DecodePlan plan;
+  mla_status st = check_decode(p, q_nope, q_pe, wkv_b, kv_cache, kv_scale, pe_cache, cache_lens,
+                               topk_idx, out, workspace, workspace_bytes, &plan);
+  if (st != MLA_OK || p->batch == 0) return st == MLA_OK ? ok() : st;
   mla::DecodeArgs d{q_nope, q_pe, wkv_b, kv_cache, kv_scale, pe_cache, cache_lens, topk_idx, out, workspace};
-  const hipError_t e = mla::launch_decode(*p, d, (hipStream_t)stream);
+  const hipError_t e = mla::launch_decode(*p, d, nullptr, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "HIP: %s", hipGetErrorString(e));
+  return ok();
+}
+
+mla_status mla_decode_step(const mla_params* p, const void* kv_new, const void* pe_new,
+                           const void* q_nope, const void* q_pe, const void* wkv_b,
+                           void* kv_cache, float* kv_scale, void* pe_cache,
+                           const int32_t* cache_lens, const int32_t* topk_idx, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  mla::DecodePlan plan;
+  mla_status st = check_decode(p, q_nope, q_pe, wkv_b, kv_cache, kv_scale, pe_cache, cache_lens,
+                               topk_idx, out, workspace, workspace_bytes, &plan);
+  if (st != MLA_OK || p->batch == 0) return st == MLA_OK ? ok() : st;
+  if (!kv_new || !pe_new) return fail(MLA_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+  if (!aligned(kv_new, 16) || !aligned(pe_new, 16))
+    return fail(MLA_ERR_INVALID_ARG, "bf16/uint8 tensors must be 16-byte aligned");
+  mla::DecodeArgs d{q_nope, q_pe, wkv_b, kv_cache, kv_scale, pe_cache, cache_lens, topk_idx, out, workspace};
+  mla::CacheWriteArgs c{kv_new, pe_new, nullptr, kv_cache, kv_scale, pe_cache};
+  const hipError_t e = mla::launch_decode(*p, d, &c, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "HIP: %s", hipGetErrorString(e));
   return ok();
 }

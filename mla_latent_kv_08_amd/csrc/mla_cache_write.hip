@@ -1,6 +1,7 @@
 // mla_cache_write.hip -- store new latent and rotary rows in the caches
 // (cache-write excerpt of "DeepSeek-V3.2-Exp . KV cache"), optionally as
 // E4M3FN codes with one fp32 scale per 128 latent elements.
+#include "mla_cache_store.hpp"
 #include "mla_device.hpp"
 #include "mla_launch.hpp"
 
@@ -19,17 +20,10 @@ __global__ __launch_bounds__(256) void cache_write_bf16_kernel(
   const int b = (int)(bi / s), i = (int)(bi % s);
   const long long r = (long long)start_pos[b] + i;
   if (r < 0 || r >= T) return;
-  const size_t row = (size_t)b * T + (size_t)r;
-  if (ch < 64) {
-    *(u32x4*)(kv + row * kC + ch * 8) = *(const u32x4*)(kv_new + (size_t)bi * kC + ch * 8);
-  } else {
-    *(u32x4*)(pe + row * kR + (ch - 64) * 8) = *(const u32x4*)(pe_new + (size_t)bi * kR + (ch - 64) * 8);
-  }
+  store_row_chunk_bf16(kv_new, pe_new, kv, pe, (size_t)bi, (size_t)b * T + (size_t)r, ch);
 }
 
-// FP8 cache: one wavefront per (sequence, new row, 128-element block); each lane
-// quantises two elements.  scale = amax / 448 and x / scale are IEEE fp32
-// divisions; the encoder rounds to nearest even and saturates.
+// FP8 cache: one wavefront per (sequence, new row, 128-element block).
 __global__ __launch_bounds__(256) void cache_write_fp8_kernel(
     const uint16_t* __restrict__ kv_new, const uint16_t* __restrict__ pe_new,
     const int32_t* __restrict__ start_pos, uint8_t* __restrict__ kv, float* __restrict__ kv_scale,
@@ -43,20 +37,7 @@ __global__ __launch_bounds__(256) void cache_write_fp8_kernel(
   const int b = (int)(bi / s), i = (int)(bi % s);
   const long long r = (long long)start_pos[b] + i;
   if (r < 0 || r >= T) return;  // uniform per wave
-  const size_t row = (size_t)b * T + (size_t)r;
-  const uint32_t x2 = *(const uint32_t*)(kv_new + (size_t)bi * kC + blk * kBlk + 2 * lane);
-  const float x0 = bf_lo(x2), x1 = bf_hi(x2);
-  const float amax = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
-  const float scale = amax / 448.0f;
-  uint32_t c0 = 0, c1 = 0;
-  if (scale != 0.0f) {
-    c0 = f32_to_e4m3fn(x0 / scale);
-    c1 = f32_to_e4m3fn(x1 / scale);
-  }
-  *(uint16_t*)(kv + row * kC + blk * kBlk + 2 * lane) = (uint16_t)(c0 | (c1 << 8));
-  if (lane == 0) kv_scale[row * 4 + blk] = scale;
-  if (blk == 0 && lane < 8)
-    *(u32x4*)(pe + row * kR + lane * 8) = *(const u32x4*)(pe_new + (size_t)bi * kR + lane * 8);
+  store_row_block_fp8(kv_new, pe_new, kv, kv_scale, pe, (size_t)bi, (size_t)b * T + (size_t)r, blk, lane);
 }
 
 hipError_t launch_cache_write(const mla_params& p, const CacheWriteArgs& c, hipStream_t stream) {

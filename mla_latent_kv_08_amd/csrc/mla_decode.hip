@@ -10,6 +10,9 @@
 //   uproj      out[b,h,:] = W_UV[h] . o[b,h,:]          (last einsum)
 #include <math.h>
 
+#include <algorithm>
+
+#include "mla_cache_store.hpp"
 #include "mla_device.hpp"
 #include "mla_launch.hpp"
 #include "mla_plan.hpp"
@@ -159,23 +162,67 @@ __device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min
 }
 
 // ---------------------------------------------------------------------------
-// absorb: grid (heads_padded + 1, 4 column blocks of 128), 256 threads.
-// Workgroup (heads_padded, 0) computes the attention work plan instead.
+// absorb: grid (heads_padded + 1 + writer columns, 4 column blocks of 128),
+// 256 threads.  Workgroup (heads_padded, 0) computes the attention work plan
+// instead; in the fused step the workgroups of the writer columns store the
+// new cache row of every sequence at position cache_lens[b] - 1 (before the
+// attention kernel, which is launched after this one, reads the caches).
 // Thread (cq = tid%16, dq = tid/16) keeps W_UK[h][8dq..8dq+7][c0..c0+7] in
 // registers and accumulates over its 8 rows of d for every sequence; the 16
 // partial sums per column are added through LDS.  Output row layout of qt:
 // [absorbed q (512) | q_pe (64)] in bf16; padded heads are zero.
 // ---------------------------------------------------------------------------
+enum RowWriteMode { kNoWrite = 0, kWriteBf16 = 1, kWriteFp8 = 2 };
+
+struct RowWrite {
+  const uint16_t* kv_new;  // [B][512]
+  const uint16_t* pe_new;  // [B][64]
+  void* kv;                // bf16 or E4M3 codes [B][T][512]
+  float* kv_scale;         // [B][T][4] for the FP8 cache
+  uint16_t* pe;            // [B][T][64]
+};
+
+// Writer workgroup w of nw: bf16 rows as 72 16-byte chunks per thread item,
+// FP8 rows as four 128-element blocks per wavefront item.
+template <int WRITE>
+__device__ __forceinline__ void write_new_rows(const RowWrite& rw, const int32_t* lens, int B, int T,
+                                               int w, int nw) {
+  const int tid = threadIdx.x;
+  if (WRITE == kWriteBf16) {
+    for (long long g = (long long)w * 256 + tid; g < (long long)B * 72; g += (long long)nw * 256) {
+      const int b = (int)(g / 72), ch = (int)(g % 72);
+      const long long r = (long long)lens[b] - 1;
+      if (r < 0 || r >= T) continue;
+      store_row_chunk_bf16(rw.kv_new, rw.pe_new, (uint16_t*)rw.kv, rw.pe, (size_t)b,
+                           (size_t)b * T + (size_t)r, ch);
+    }
+  } else if (WRITE == kWriteFp8) {
+    const int lane = tid & 63;
+    for (long long g = (long long)w * 4 + (tid >> 6); g < (long long)B * 4; g += (long long)nw * 4) {
+      const int b = (int)(g >> 2), blk = (int)(g & 3);
+      const long long r = (long long)lens[b] - 1;
+      if (r < 0 || r >= T) continue;  // uniform per wave
+      store_row_block_fp8(rw.kv_new, rw.pe_new, (uint8_t*)rw.kv, rw.kv_scale, rw.pe, (size_t)b,
+                          (size_t)b * T + (size_t)r, blk, lane);
+    }
+  }
+}
+
+template <int WRITE>
 __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict__ q_nope,
                                                      const uint16_t* __restrict__ q_pe,
                                                      const uint16_t* __restrict__ wkv_b,
                                                      uint16_t* __restrict__ qt, int B, int H,
                                                      int Hp, const int32_t* __restrict__ lens,
                                                      int T, int topk, int min_group_tiles,
-                                                     int G, int32_t* wcum, int4* rec) {
+                                                     int G, int32_t* wcum, int4* rec, RowWrite rw) {
   const int h = blockIdx.x, cblk = blockIdx.y, tid = threadIdx.x;
   if (h == Hp) {
     if (cblk == 0) plan_groups(lens, B, T, topk, min_group_tiles, G, wcum, rec);
+    return;
+  }
+  if (WRITE != kNoWrite && h > Hp) {
+    write_new_rows<WRITE>(rw, lens, B, T, (h - Hp - 1) * 4 + cblk, (gridDim.x - Hp - 1) * 4);
     return;
   }
   const int cq = tid & 15, dq = tid >> 4;
@@ -1100,7 +1147,8 @@ __global__ __launch_bounds__(64) void uproj_kernel(const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, hipStream_t stream) {
+hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWriteArgs* write,
+                         hipStream_t stream) {
   const DecodePlan plan = make_decode_plan(p);
   const int B = p.batch, H = p.num_heads;
   char* ws = (char*)d.workspace;
@@ -1114,10 +1162,23 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, hipStream_t s
   int32_t* wcum = (int32_t*)(ws + plan.off_wcum);
   int4* rec = (int4*)(ws + plan.off_rec);
 
-  err = launch_kernel(absorb_kernel, dim3(plan.heads_padded + 1, 4), dim3(256), stream, evk(0),
-                      (const uint16_t*)d.q_nope, (const uint16_t*)d.q_pe, (const uint16_t*)d.wkv_b,
-                      qt, B, H, plan.heads_padded, d.cache_lens, p.max_seq_len, p.topk,
-                      plan.min_group_tiles, (int)plan.max_groups, wcum, rec);
+  const bool fp8 = p.kv_dtype == MLA_KV_FP8_E4M3_B128, topk = p.topk > 0;
+  RowWrite rw{};
+  int write_cols = 0;
+  auto absorb = absorb_kernel<kNoWrite>;
+  if (write) {
+    rw = RowWrite{(const uint16_t*)write->kv_new, (const uint16_t*)write->pe_new, write->kv_cache,
+                  write->kv_scale, (uint16_t*)write->pe_cache};
+    // about one item per thread (bf16) or per wavefront (FP8), at most 64 columns
+    const long long items_per_col = fp8 ? 16 : 1024, items = (long long)B * (fp8 ? 4 : 72);
+    write_cols = (int)std::min<long long>((items + items_per_col - 1) / items_per_col, 64);
+    absorb = fp8 ? absorb_kernel<kWriteFp8> : absorb_kernel<kWriteBf16>;
+  }
+  err = launch_kernel(absorb, dim3(plan.heads_padded + 1 + write_cols, 4), dim3(256), stream,
+                      evk(0), (const uint16_t*)d.q_nope, (const uint16_t*)d.q_pe,
+                      (const uint16_t*)d.wkv_b, qt, B, H, plan.heads_padded, d.cache_lens,
+                      p.max_seq_len, p.topk, plan.min_group_tiles, (int)plan.max_groups, wcum, rec,
+                      rw);
   if (err != hipSuccess) return err;
 
   AttnArgs aa;
@@ -1137,7 +1198,6 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, hipStream_t s
   aa.head_blocks = plan.head_blocks;
   aa.scale_log2 = p.softmax_scale * 1.4426950408889634f;
   const dim3 agrid((unsigned)plan.max_groups);
-  const bool fp8 = p.kv_dtype == MLA_KV_FP8_E4M3_B128, topk = p.topk > 0;
   auto attn = fp8 ? (topk ? attn_kernel<true, true> : attn_kernel<true, false>)
                   : (topk ? attn_kernel<false, true> : attn_kernel<false, false>);
   err = launch_kernel(attn, agrid, dim3(kAttnThreads), stream, evk(1), aa);

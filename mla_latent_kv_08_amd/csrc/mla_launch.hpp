@@ -31,7 +31,10 @@ struct CacheWriteArgs {
   void* pe_cache;
 };
 
-hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, hipStream_t stream);
+// With `write` non-null (the fused decode step) the new row of each sequence is
+// stored at position cache_lens[b] - 1 before the attention reads the caches.
+hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWriteArgs* write,
+                         hipStream_t stream);
 
 // Launch `kernel` on `stream`.  With `ev` non-null the start and end of the
 // dispatch are stamped into ev[0] and ev[1] by the dispatch itself (no extra

@@ -56,6 +56,8 @@ def _load():
     L.mla_decode_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     L.mla_decode.restype = ctypes.c_int
     L.mla_decode.argtypes = [P] + [vp] * 10 + [ctypes.c_size_t, vp]
+    L.mla_decode_step.restype = ctypes.c_int
+    L.mla_decode_step.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, vp]
     L.mla_status_string.restype = ctypes.c_char_p
     L.mla_status_string.argtypes = [ctypes.c_int]
     L.mla_last_error.restype = ctypes.c_char_p
@@ -135,4 +137,33 @@ def decode(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, kv_scale=None, t
     _check(lib.mla_decode(ctypes.byref(p), _ptr(q_nope), _ptr(q_pe), _ptr(wkv_b), _ptr(kv_cache),
                           _ptr(kv_scale), _ptr(pe_cache), _ptr(cache_lens), _ptr(topk_idx),
                           _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def decode_step(kv_new, pe_new, q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens,
+                kv_scale=None, topk_idx=None, out=None, workspace=None,
+                softmax_scale=DEFAULT_SOFTMAX_SCALE, stream=None, trace_events=None):
+    """mla_decode_step: store row cache_lens[b] - 1, then decode; returns out.
+
+    kv_new [B,1,512] and pe_new [B,1,64] bf16; every other argument as for
+    decode (the caches are written).
+    """
+    _dev(kv_new, pe_new, q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, kv_scale, topk_idx,
+         out, workspace)
+    B, H = q_nope.shape[0], q_nope.shape[2]
+    if kv_new.shape[0] != B or pe_new.shape[0] != B:
+        raise ValueError("kv_new and pe_new need one row per sequence")
+    fp8 = kv_scale is not None
+    k = 0 if topk_idx is None else topk_idx.shape[-1]
+    p = make_params(B, H, kv_cache.shape[1], KV_FP8_E4M3_B128 if fp8 else KV_BF16, topk=k,
+                    softmax_scale=softmax_scale, trace_events=trace_events)
+    if out is None:
+        out = torch.empty(B, 1, H, D_V, dtype=torch.bfloat16, device=q_nope.device)
+    if workspace is None:
+        workspace = torch.empty(max(decode_workspace_size(p), 16), dtype=torch.uint8,
+                                device=q_nope.device)
+    _check(lib.mla_decode_step(ctypes.byref(p), _ptr(kv_new), _ptr(pe_new), _ptr(q_nope),
+                               _ptr(q_pe), _ptr(wkv_b), _ptr(kv_cache), _ptr(kv_scale),
+                               _ptr(pe_cache), _ptr(cache_lens), _ptr(topk_idx), _ptr(out),
+                               _ptr(workspace), workspace.numel(), _stream(stream)))
     return out

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(m):
     names = declared_functions()
-    assert {"mla_cache_write", "mla_decode", "mla_decode_workspace_size",
+    assert {"mla_cache_write", "mla_decode", "mla_decode_step", "mla_decode_workspace_size",
             "mla_status_string", "mla_last_error", "mla_abi_version"} <= set(names)
     for n in names:
         assert hasattr(m.lib, n), n
@@ -122,3 +122,22 @@ def test_workspace_size_is_host_only_and_monotone(m):
     assert m.decode_workspace_size(m.make_params(8, 128, 65536, topk=65536)) > small_k
     with pytest.raises(m.MLAError):
         m.decode_workspace_size(m.make_params(8, 200, 4096))
+
+
+def test_decode_step_rejects_bad_arguments(m):
+    P = m.make_params
+
+    def step(p, kv_new=FAKE, pe_new=FAKE, ws_bytes=1 << 40, **kw):
+        a = dict(q_nope=FAKE, q_pe=FAKE, wkv_b=FAKE, kv=FAKE, scale=None, pe=FAKE, lens=FAKE,
+                 topk=None, out=FAKE, ws=FAKE)
+        a.update(kw)
+        return m.lib.mla_decode_step(ctypes.byref(p), kv_new, pe_new, a["q_nope"], a["q_pe"],
+                                     a["wkv_b"], a["kv"], a["scale"], a["pe"], a["lens"],
+                                     a["topk"], a["out"], a["ws"], ws_bytes, None)
+
+    assert step(P(1, 16, 100), kv_new=None) == 1
+    assert step(P(1, 16, 100), pe_new=ctypes.c_void_p(0x100004)) == 1      # misaligned
+    assert step(P(1, 16, 100, kv_dtype=1)) == 1                             # fp8 without scales
+    assert step(P(1, 16, 100, seqlen_q=2)) == 2
+    assert step(P(1, 16, 100), ws_bytes=16) == 3
+    assert step(P(0, 16, 100), kv_new=None) == 0                            # empty batch: no-op

@@ -239,3 +239,58 @@ def test_workload_full_sampled(m, name):
     w = synth.WORKLOADS[name]
     x = synth.make_inputs(w)
     run_case(m, w, x, pairs=sample_pairs(w, 64, w.seed), label=name)
+
+
+# ---------------------------------------------------------------- fused decode step
+
+def _upload_caches(m, w, x):
+    """Device copies of the host caches of x (FP8: the oracle's codes and scales)."""
+    if not w.fp8:
+        return x["kv"].clone(), None, x["pe"].clone()
+    codes, scales, pe = oracle.cache_write(x["kv"], x["pe"], torch.zeros(w.batch, dtype=torch.int32),
+                                           w.max_seq_len, True)
+    return torch.from_numpy(codes), torch.from_numpy(scales), torch.from_numpy(pe.view(np.int16)).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("fp8,topk,B", [(False, 0, 5), (True, 0, 5), (False, 96, 3), (True, 0, 2100),
+                                        (False, 0, 2100)])
+def test_decode_step_writes_then_attends(m, fp8, topk, B):
+    T = 70 if B > 100 else 300
+    w = synth.Workload("step", B, 16 if B > 100 else 128, T, fp8=fp8, topk=topk, ragged=(0, T), seed=12 + B)
+    x = synth.make_inputs(w)
+    lens = x["cache_lens"].clone()
+    lens[0] = 0              # nothing written, empty attention
+    lens[1] = T              # row T - 1 written
+    if B > 2:
+        lens[2] = T + 5      # row outside the buffer: dropped, attention over T rows
+    x["cache_lens"] = lens
+    g = torch.Generator().manual_seed(13)
+    kv_new = torch.randn(B, 1, 512, generator=g).to(torch.bfloat16)
+    pe_new = torch.randn(B, 1, 64, generator=g).to(torch.bfloat16)
+    kv_h, sc_h, pe_h = _upload_caches(m, w, x)
+    kv, sc, pe = to_dev(kv_h), to_dev(sc_h), to_dev(pe_h)
+    print(f"[step] B={B} T={T} fp8={fp8} topk={topk}", flush=True)
+    args = [to_dev(x["q_nope"]), to_dev(x["q_pe"]), to_dev(x["wkv_b"])]
+    out = m.decode_step(to_dev(kv_new), to_dev(pe_new), *args, kv, pe, to_dev(lens), kv_scale=sc,
+                        topk_idx=to_dev(x["topk_idx"]))
+    torch.cuda.synchronize()
+    # caches: the oracle's cache write at start_pos = cache_lens - 1 on the same old caches
+    okv, osc, ope = oracle.cache_write(kv_new, pe_new, (lens - 1).to(torch.int32), T, fp8,
+                                       kv_cache=kv_h.numpy().copy() if fp8 else kv_h.view(torch.int16).numpy().view(np.uint16).copy(),
+                                       kv_scale=None if sc_h is None else sc_h.numpy().copy(),
+                                       pe_cache=pe_h.view(torch.int16).numpy().view(np.uint16).copy())
+    got_kv = kv.cpu().numpy() if fp8 else kv.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got_kv, okv), "latent cache differs"
+    assert np.array_equal(pe.cpu().view(torch.int16).numpy().view(np.uint16), ope), "rotary cache differs"
+    if fp8:
+        assert np.array_equal(sc.cpu().numpy().view(np.uint32), osc.view(np.uint32)), "scales differ"
+    ref = oracle.decode(x["q_nope"], x["q_pe"], x["wkv_b"], okv, ope, lens, synth.SOFTMAX_SCALE,
+                        kv_scale=osc, topk_idx=x["topk_idx"])
+    check(out, ref.reshape(B, 1, w.heads, 128), fp8, f"step B{B} fp8={fp8} topk={topk}")
+    assert (out[0].float() == 0).all()
+    # the same as the two separate calls on the GPU, bit for bit
+    kv2, sc2, pe2 = to_dev(kv_h), to_dev(sc_h), to_dev(pe_h)
+    m.cache_write(to_dev(kv_new), to_dev(pe_new), to_dev((lens - 1).to(torch.int32)), kv2, pe2,
+                  kv_scale=sc2)
+    out2 = m.decode(*args, kv2, pe2, to_dev(lens), kv_scale=sc2, topk_idx=to_dev(x["topk_idx"]))
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
