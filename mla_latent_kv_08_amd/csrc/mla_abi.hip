@@ -100,7 +100,7 @@ mla_status mla_decode_workspace_size(const mla_params* p, size_t* bytes) {
   if (p->topk < 0 || p->topk > p->max_seq_len)
     return fail(MLA_ERR_INVALID_ARG, "topk = %d outside 0..max_seq_len", p->topk);
   const mla::DecodePlan plan = mla::make_decode_plan(*p);
-  if (plan.max_groups > 0x7FFFFFFFLL || plan.max_groups * p->num_heads > (1LL << 40))
+  if (plan.max_groups > 0x7FFFFFFFLL || plan.max_groups * plan.heads_padded > (1LL << 40))
     return fail(MLA_ERR_UNSUPPORTED, "too many attention workgroups for this batch and top-k");
   *bytes = plan.bytes;
   return ok();
@@ -141,7 +141,7 @@ mla_status check_decode(const mla_params* p, const void* q_nope, const void* q_p
   if (!aligned(cache_lens, 4) || (kv_scale && !aligned(kv_scale, 4)) || (topk_idx && !aligned(topk_idx, 4)))
     return fail(MLA_ERR_INVALID_ARG, "int32/fp32 tensors must be 4-byte aligned");
   *plan = mla::make_decode_plan(*p);
-  if (plan->max_groups > 0x7FFFFFFFLL || plan->max_groups * p->num_heads > (1LL << 40))
+  if (plan->max_groups > 0x7FFFFFFFLL || plan->max_groups * plan->heads_padded > (1LL << 40))
     return fail(MLA_ERR_UNSUPPORTED, "too many attention workgroups for this batch and top-k");
   if (!workspace || workspace_bytes < plan->bytes)
     return fail(MLA_ERR_WORKSPACE, "workspace needs %zu bytes, got %zu", plan->bytes,

@@ -29,38 +29,57 @@ __device__ __forceinline__ int selected_entries(int len, int topk) {
   return topk > 0 ? (len > 0 ? topk : 0) : len;
 }
 
-// Inclusive prefix sum over the 256 threads of a workgroup; *total receives
-// the sum of all 256 values.
+// Inclusive prefix sum over the 256 threads of a workgroup (wavefront
+// shuffles, then the four wave totals through LDS); *total receives the sum
+// of all 256 values.  sc: 4 ints of LDS.
 __device__ int block_scan_256(int v, int* sc, int* total) {
-  const int tid = threadIdx.x;
-  sc[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int y = tid >= off ? sc[tid - off] : 0;
-    __syncthreads();
-    sc[tid] += y;
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
   }
-  const int r = sc[tid];
-  *total = sc[255];
+  if (lane == 63) sc[w] = v;
   __syncthreads();
-  return r;
+  const int s0 = sc[0], s1 = sc[1], s2 = sc[2], s3 = sc[3];
+  __syncthreads();  // sc free for the next call
+  *total = s0 + s1 + s2 + s3;
+  return v + (w > 0 ? s0 : 0) + (w > 1 ? s1 : 0) + (w > 2 ? s2 : 0);
 }
 
-// Sum (or max) over the 256 threads of a workgroup, returned to every thread.
-template <bool MAX>
-__device__ long long block_reduce_256(long long v, long long* red) {
+// Sum, maximum and sum over the 256 threads of a workgroup, in one pass,
+// returned to every thread.  red: 12 long longs of LDS.
+__device__ void block_reduce3_256(long long& a, long long& m, long long& c, long long* red) {
   const int tid = threadIdx.x;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
-    const long long y = __shfl_xor(v, o, 64);
-    v = MAX ? (y > v ? y : v) : v + y;
+    a += __shfl_xor(a, o, 64);
+    const long long y = __shfl_xor(m, o, 64);
+    m = y > m ? y : m;
+    c += __shfl_xor(c, o, 64);
   }
+  if ((tid & 63) == 0) {
+    red[3 * (tid >> 6)] = a;
+    red[3 * (tid >> 6) + 1] = m;
+    red[3 * (tid >> 6) + 2] = c;
+  }
+  __syncthreads();
+  a = red[0] + red[3] + red[6] + red[9];
+  m = red[1];
+#pragma unroll
+  for (int k = 1; k < 4; ++k) m = red[3 * k + 1] > m ? red[3 * k + 1] : m;
+  c = red[2] + red[5] + red[8] + red[11];
+  __syncthreads();
+}
+
+// Sum over the 256 threads of a workgroup, returned to every thread.
+__device__ long long block_sum_256(long long v, long long* red) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   if ((tid & 63) == 0) red[tid >> 6] = v;
   __syncthreads();
-  long long r = red[0];
-#pragma unroll
-  for (int k = 1; k < 4; ++k) r = MAX ? (red[k] > r ? red[k] : r) : r + red[k];
+  const long long r = red[0] + red[1] + red[2] + red[3];
   __syncthreads();
   return r;
 }
@@ -73,12 +92,29 @@ constexpr int kPlanCache = 2048;  // per-sequence values kept in LDS by the plan
 // each of the G attention workgroups, the record {sequence, first tile, end
 // tile, clamped length} (sequence -1: workgroup unused), so that a workgroup
 // starts from one 16-byte load.
+// floor(a / b) and ceil(a / b) for 0 <= a < 2^52 and b >= 1.  Both are
+// exact in double, and a non-integer quotient a/b lies at least 1/b from the
+// nearest integer n, more than half an ulp of n (n * 2^-53 < 1/b because
+// n * b <= a + b < 2^53), so rounding never lands on n: floor and ceil of the
+// correctly rounded quotient are exact, and far cheaper than a 64-bit integer
+// division.
+__device__ __forceinline__ long long floor_div(long long a, long long b) {
+  return (long long)floor((double)a / (double)b);
+}
+__device__ __forceinline__ long long ceil_div(long long a, long long b) {
+  return (long long)ceil((double)a / (double)b);
+}
+
+// LDS of the planner (the caller's buffer, kPlanLdsBytes).
+constexpr int kPlanLdsBytes = 12 * 8 + 4 * 4 + (3 * kPlanCache + 1) * 4 + 32 * 4;
+
 __device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min_tiles, int G,
-                            int32_t* wcum, int4* rec) {
-  __shared__ int tl[kPlanCache];       // tiles of sequence b
-  __shared__ int sw[kPlanCache + 1];   // first workgroup of sequence b
-  __shared__ int sc[256];
-  __shared__ long long red[4];
+                            int32_t* wcum, int4* rec, char* lds) {
+  long long* red = (long long*)lds;           // [12]
+  int* sc = (int*)(lds + 96);                 // [4]
+  int* tl = sc + 4;                           // [kPlanCache] tiles of sequence b
+  int* sl = tl + kPlanCache;                  // [kPlanCache] clamped length of sequence b
+  int* sw = sl + kPlanCache;                  // [kPlanCache + 1] first workgroup of sequence b
   const int tid = threadIdx.x;
   auto tiles_of = [&](int bb) -> int {
     return (selected_entries(seq_len(lens, bb, T), topk) + kTileRows - 1) / kTileRows;
@@ -86,35 +122,64 @@ __device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min
   auto tiles = [&](int bb) -> int { return bb < kPlanCache ? tl[bb] : tiles_of(bb); };
   long long tot = 0, mx = 0, nonempty = 0;
   for (int bb = tid; bb < B; bb += 256) {
-    const int t = tiles_of(bb);
-    if (bb < kPlanCache) tl[bb] = t;
+    const int len = seq_len(lens, bb, T);
+    const int t = (selected_entries(len, topk) + kTileRows - 1) / kTileRows;
+    if (bb < kPlanCache) {
+      tl[bb] = t;
+      sl[bb] = len;
+    }
     tot += t;
     mx = t > mx ? t : mx;
     nonempty += t > 0;
   }
-  __syncthreads();
-  tot = block_reduce_256<false>(tot, red);
-  mx = block_reduce_256<true>(mx, red);
-  nonempty = block_reduce_256<false>(nonempty, red);
-  // workgroups needed with budget S
-  auto groups_for = [&](long long S) -> long long {
-    long long c = 0;
-    for (int bb = tid; bb < B; bb += 256) c += (tiles(bb) + S - 1) / S;
-    return block_reduce_256<false>(c, red);
-  };
+  block_reduce3_256(tot, mx, nonempty, red);  // (its barrier also publishes tl, sl)
   long long S = mx > 0 ? mx : 1;
   if (mx > 0 && nonempty < kTargetCUs) {
     // sum ceil(t_b / S) <= tot / S + nonempty, so S = ceil(tot / (256 - nonempty))
-    // fits, and nothing below ceil(tot / 256) does: search between the two
+    // fits, and nothing below ceil(tot / 256) does: search between the two.
+    // Every S searched is >= tot / 256 and <= mx < 2^26, so the counts stay
+    // below 256 + B and 32-bit arithmetic suffices.
     long long lo = (tot + kTargetCUs - 1) / kTargetCUs;
-    long long hi = (tot + (kTargetCUs - nonempty) - 1) / (kTargetCUs - nonempty);
+    long long hi = ceil_div(tot, kTargetCUs - nonempty);
     if (lo < 1) lo = 1;
     if (hi > mx) hi = mx;  // S = mx gives one workgroup per sequence, which fits
     if (lo > hi) lo = hi;
-    while (lo < hi) {  // smallest S in [lo, hi] that fits (groups_for is non-increasing)
-      const long long mid = (lo + hi) / 2;
-      if (groups_for(mid) <= kTargetCUs) hi = mid;
-      else lo = mid + 1;
+    int* cnt = sc + 4 + 3 * kPlanCache + 1;  // [4][8] wave partial counts
+    while (lo < hi) {
+      // smallest S in [lo, hi] that fits (the count is non-increasing in S):
+      // test 8 budgets spread over [lo, hi) in one pass
+      const long long span = hi - lo;
+      uint32_t cand[8];
+      int c[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        cand[i] = (uint32_t)(lo + (span <= 8 ? (i < span ? i : span - 1) : span * i / 8));
+        c[i] = 0;
+      }
+      for (int bb = tid; bb < B; bb += 256) {
+        const uint32_t t = (uint32_t)tiles(bb);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] += (int)ceil_div(t, cand[i]);
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] += __shfl_xor(c[i], o, 64);
+      }
+      if ((tid & 63) == 0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cnt[8 * (tid >> 6) + i] = c[i];
+      }
+      __syncthreads();
+      long long nlo = lo, nhi = hi;
+      for (int i = 7; i >= 0; --i) {  // candidates ascend: bracket the first that fits
+        const int tot_i = cnt[i] + cnt[8 + i] + cnt[16 + i] + cnt[24 + i];
+        if (tot_i <= kTargetCUs) nhi = cand[i];
+        else if ((long long)cand[i] + 1 > nlo) nlo = (long long)cand[i] + 1;
+      }
+      __syncthreads();
+      lo = nlo;
+      hi = nhi < lo ? lo : nhi;
     }
     S = lo;
   }
@@ -123,7 +188,7 @@ __device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min
   int run = 0, total;
   for (int base = 0; base < B; base += 256) {
     const int bb = base + tid;
-    const int k = bb < B ? (int)((tiles(bb) + S - 1) / S) : 0;
+    const int k = bb < B ? (int)ceil_div(tiles(bb), S) : 0;
     const int incl = block_scan_256(k, sc, &total);
     if (bb < B) {
       wcum[bb + 1] = run + incl;
@@ -132,7 +197,7 @@ __device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min
         const int t = tiles_of(bb), len = seq_len(lens, bb, T);
         for (int p = 0; p < k; ++p)
           rec[run + incl - k + p] =
-              make_int4(bb, (int)((long long)p * t / k), (int)((long long)(p + 1) * t / k), len);
+              make_int4(bb, (int)floor_div((long long)p * t, k), (int)floor_div((long long)(p + 1) * t, k), len);
       }
     }
     run += total;
@@ -156,22 +221,11 @@ __device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min
       else hi = mid - 1;
     }
     const int t = tl[lo], k = sw[lo + 1] - sw[lo], p = i - sw[lo];
-    rec[i] = make_int4(lo, (int)((long long)p * t / k), (int)((long long)(p + 1) * t / k), seq_len(lens, lo, T));
+    rec[i] = make_int4(lo, (int)floor_div((long long)p * t, k), (int)floor_div((long long)(p + 1) * t, k), sl[lo]);
   }
   for (int i = run + tid; i < G; i += 256) rec[i] = make_int4(-1, 0, 0, 0);
 }
 
-// ---------------------------------------------------------------------------
-// absorb: grid (heads_padded + 1 + writer columns, 4 column blocks of 128),
-// 256 threads.  Workgroup (heads_padded, 0) computes the attention work plan
-// instead; in the fused step the workgroups of the writer columns store the
-// new cache row of every sequence at position cache_lens[b] - 1 (before the
-// attention kernel, which is launched after this one, reads the caches).
-// Thread (cq = tid%16, dq = tid/16) keeps W_UK[h][8dq..8dq+7][c0..c0+7] in
-// registers and accumulates over its 8 rows of d for every sequence; the 16
-// partial sums per column are added through LDS.  Output row layout of qt:
-// [absorbed q (512) | q_pe (64)] in bf16; padded heads are zero.
-// ---------------------------------------------------------------------------
 enum RowWriteMode { kNoWrite = 0, kWriteBf16 = 1, kWriteFp8 = 2 };
 
 struct RowWrite {
@@ -208,76 +262,100 @@ __device__ __forceinline__ void write_new_rows(const RowWrite& rw, const int32_t
   }
 }
 
+// ---------------------------------------------------------------------------
+// absorb: grid (heads_padded + 1 + writer columns, 4 column blocks of 128,
+// sequence ranges), 256 threads.  Workgroup (heads_padded, 0, 0) computes the
+// attention work plan instead; in the fused step the workgroups of the writer
+// columns (z = 0) store the new cache row of every sequence at position
+// cache_lens[b] - 1 (before the attention kernel, which is launched after
+// this one, reads the caches).
+//
+// Head h, columns 128y..128y+127: the W_UK slice (128 d x 128 c) is staged in
+// LDS and held as MFMA B fragments, wave w taking 32 columns; each block of 32
+// sequences is one 32x32 tile per wave (8 MFMAs over d), staged through LDS
+// and stored into qt in the attention kernel's fragment order:
+//   qt[b][head block hb][k-step st][lane][8], lane = 32 g + (h % 32),
+// holding the absorbed-query / q_pe elements 16 st + 8 g .. +7 of head
+// 32 hb + (h % 32), so that each of the attention's query loads reads 1 KB
+// contiguous per wave.  Padded heads are zero.
+// ---------------------------------------------------------------------------
 template <int WRITE>
 __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict__ q_nope,
                                                      const uint16_t* __restrict__ q_pe,
                                                      const uint16_t* __restrict__ wkv_b,
                                                      uint16_t* __restrict__ qt, int B, int H,
-                                                     int Hp, const int32_t* __restrict__ lens,
+                                                     int Hp, int bz, const int32_t* __restrict__ lens,
                                                      int T, int topk, int min_group_tiles,
                                                      int G, int32_t* wcum, int4* rec, RowWrite rw) {
+  // one LDS buffer: the planner's arrays, or the W_UK tile, whose space the
+  // output tile reuses once the fragments are in registers
+  constexpr int kWRow = 128 + 8;  // padded tile rows (bf16)
+  constexpr int kLds = 128 * kWRow * 2 > kPlanLdsBytes ? 128 * kWRow * 2 : kPlanLdsBytes;
+  __shared__ __attribute__((aligned(16))) char smem[kLds];
   const int h = blockIdx.x, cblk = blockIdx.y, tid = threadIdx.x;
-  if (h == Hp) {
-    if (cblk == 0) plan_groups(lens, B, T, topk, min_group_tiles, G, wcum, rec);
+  if (h >= Hp) {
+    if (blockIdx.z != 0) return;
+    if (h == Hp) {
+      if (cblk == 0) plan_groups(lens, B, T, topk, min_group_tiles, G, wcum, rec, smem);
+    } else if (WRITE != kNoWrite) {
+      write_new_rows<WRITE>(rw, lens, B, T, (h - Hp - 1) * 4 + cblk, (gridDim.x - Hp - 1) * 4);
+    }
     return;
   }
-  if (WRITE != kNoWrite && h > Hp) {
-    write_new_rows<WRITE>(rw, lens, B, T, (h - Hp - 1) * 4 + cblk, (gridDim.x - Hp - 1) * 4);
-    return;
-  }
-  const int cq = tid & 15, dq = tid >> 4;
-  const int c0 = cblk * 128 + cq * 8;
+  const int b_lo = blockIdx.z * bz, b_hi = min(B, b_lo + bz);
+  const int HB = Hp >> 5, hb = h >> 5, hn = h & 31;
+  // element offset of chunk (8 values from c, c % 8 == 0) of (b, h) in qt
+  auto frag = [&](int b, int c) -> size_t {
+    return (((size_t)b * HB + hb) * 36 + (c >> 4)) * 512 + (((c >> 3) & 1) * 32 + hn) * 8;
+  };
   if (h >= H) {  // padding heads: zero rows (the attention waves read them)
-    for (int b = 0; b < B; ++b) {
-      uint16_t* row = qt + ((size_t)b * Hp + h) * kQK;
-      if (tid < 16) *(u32x4*)(row + cblk * 128 + tid * 8) = u32x4{0, 0, 0, 0};
-      if (cblk == 0 && tid >= 16 && tid < 24) *(u32x4*)(row + kC + (tid - 16) * 8) = u32x4{0, 0, 0, 0};
+    const int per_b = cblk == 0 ? 24 : 16;
+    for (int i = tid; i < (b_hi - b_lo) * per_b; i += 256) {
+      const int b = b_lo + i / per_b, ch = i % per_b;
+      const int c = ch < 16 ? cblk * 128 + 8 * ch : kC + 8 * (ch - 16);
+      *(u32x4*)(qt + frag(b, c)) = u32x4{0, 0, 0, 0};
     }
     return;
   }
-  __shared__ float red[16][128 + 4];
-  float w[8][8];
+  uint16_t(*sW)[kWRow] = (uint16_t(*)[kWRow])smem;  // W_UK[h][d][128y + c]
+  uint16_t(*sD)[kWRow] = (uint16_t(*)[kWRow])smem;  // output tile [b][c], after the fragments
+  for (int i = tid; i < 128 * 16; i += 256) {
+    const int r = i >> 4, ch = i & 15;
+    *(u32x4*)&sW[r][8 * ch] = *(const u32x4*)(wkv_b + ((size_t)h * (kDN + kDV) + r) * kC + cblk * 128 + 8 * ch);
+  }
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  const int cc = 32 * wave + (lane & 31), kg = lane >> 5;
+  u32x4 bw[8];  // B[k = d][n = c]: lane holds d = 16 ks + 8 kg + j of column cc
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const u32x4 v = *(const u32x4*)(wkv_b + ((size_t)h * (kDN + kDV) + dq * 8 + i) * kC + c0);
+  for (int ks = 0; ks < 8; ++ks) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      w[i][2 * j] = bf_lo(v[j]);
-      w[i][2 * j + 1] = bf_hi(v[j]);
+    for (int j = 0; j < 4; ++j)
+      bw[ks][j] = (uint32_t)sW[16 * ks + 8 * kg + 2 * j][cc] | ((uint32_t)sW[16 * ks + 8 * kg + 2 * j + 1][cc] << 16);
+  }
+  for (int b0 = b_lo; b0 < b_hi; b0 += 32) {
+    const int bb = b0 + (lane & 31);
+    const bool ok = bb < b_hi;
+    const uint16_t* qrow = q_nope + ((size_t)(ok ? bb : b_lo) * H + h) * kDN + 8 * kg;
+    u32x4 av[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) av[ks] = ok ? *(const u32x4*)(qrow + 16 * ks) : u32x4{0, 0, 0, 0};
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) acc = mfma32(av[ks], bw[ks], acc);
+    __syncthreads();  // fragments read (first block) / sD read (later blocks)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sD[8 * (e >> 2) + 4 * kg + (e & 3)][cc] = (uint16_t)f2bf(acc[e]);
+    __syncthreads();
+    for (int i = tid; i < 32 * 16; i += 256) {
+      const int r = i >> 4, ch = i & 15;
+      if (b0 + r < b_hi) *(u32x4*)(qt + frag(b0 + r, cblk * 128 + 8 * ch)) = *(const u32x4*)&sD[r][8 * ch];
     }
   }
-  for (int b = 0; b < B; ++b) {
-    const u32x4 qv = *(const u32x4*)(q_nope + ((size_t)b * H + h) * kDN + dq * 8);
-    float q[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      q[2 * j] = bf_lo(qv[j]);
-      q[2 * j + 1] = bf_hi(qv[j]);
-    }
-    float acc[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float s = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s = fmaf(q[i], w[i][e], s);
-      acc[e] = s;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) red[dq][cq * 8 + e] = acc[e];
-    __syncthreads();
-    if (tid < 128) {
-      float s = 0.f;
-#pragma unroll
-      for (int k = 0; k < 16; ++k) s += red[k][tid];
-      qt[((size_t)b * Hp + h) * kQK + cblk * 128 + tid] = (uint16_t)f2bf(s);
-    }
-    __syncthreads();
-  }
-  if (cblk == 0) {  // copy q_pe rows (8 x 16 B per sequence)
-    for (int i = tid; i < 8 * B; i += 256) {
-      const int b = i >> 3, part = i & 7;
-      *(u32x4*)(qt + ((size_t)b * Hp + h) * kQK + kC + part * 8) =
-          *(const u32x4*)(q_pe + ((size_t)b * H + h) * kR + part * 8);
+  if (cblk == 0) {  // q_pe: elements 512..575
+    for (int i = tid; i < 8 * (b_hi - b_lo); i += 256) {
+      const int b = b_lo + (i >> 3), part = i & 7;
+      *(u32x4*)(qt + frag(b, kC + 8 * part)) = *(const u32x4*)(q_pe + ((size_t)b * H + h) * kR + 8 * part);
     }
   }
 }
@@ -331,8 +409,13 @@ constexpr int kAttnThreads = 64 * kAttnWaves;
 constexpr int kPStride = 40;                // bf16 per sP row (32 + 8 padding)
 constexpr int kScoreAhead = 4;              // score operand reads issued ahead of their MFMA
 constexpr int kOStride = 520;               // bf16 per staged output row (512 + 8 padding)
-constexpr int kFp8Codes = kTT * kC;                       // bytes of latent codes per tile
-constexpr int kFp8Stage = kFp8Codes + kTT * 16 + kTT * kR * 2;  // + scales + rotary rows
+// FP8 staging region of one wave: latent block `wave` (128 codes) of the 32
+// rows of a tile, the 32 rows' four scales, and rotary rows 8 wave .. +7.
+constexpr int kFp8WaveCodes = kTT * kBlk;                   // 4096
+constexpr int kFp8WaveScales = kTT * 4;                     // 128
+constexpr int kFp8WaveRope = 8 * kR * 2;                    // 1024
+constexpr int kFp8Wave = kFp8WaveCodes + kFp8WaveScales + kFp8WaveRope;
+constexpr int kFp8Stage = 4 * kFp8Wave;
 static_assert(32 * kOStride <= kTileElems, "a 32-head block of O fits one ring slot");
 
 struct AttnArgs {
@@ -368,6 +451,22 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 template <int OFF>
 __device__ __forceinline__ void lds_dma16(const void* src, uint32_t base) {
   asm volatile("s_add_u32 m0, %1, %2\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base), "i"(OFF)
+               : "memory", "m0", "scc");
+}
+
+// 4-byte global -> LDS copy for each lane (lane l's dword at base + OFF + 4 l),
+// issued after `dep` is available.
+template <int OFF>
+__device__ __forceinline__ void lds_dma4_after(const void* src, uint32_t base, uint32_t dep) {
+  asm volatile("s_add_u32 m0, %1, %2\n\tglobal_load_lds_dword %0, off" ::"v"(src), "s"(base), "i"(OFF), "v"(dep)
+               : "memory", "m0", "scc");
+}
+
+// lds_dma16 issued after `dep` is available: when dep was read from the LDS
+// bytes this load overwrites, that read has completed first.
+template <int OFF>
+__device__ __forceinline__ void lds_dma16_after(const void* src, uint32_t base, uint32_t dep) {
+  asm volatile("s_add_u32 m0, %1, %2\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base), "i"(OFF), "v"(dep)
                : "memory", "m0", "scc");
 }
 
@@ -416,7 +515,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sT2[kTileElems];
   __shared__ __attribute__((aligned(16))) uint16_t sP[2 * 128 * kPStride];  // by tile parity
   __shared__ float sAlpha[2 * 128];                                          // by tile parity
-  __shared__ float sL[128];
   __shared__ uint32_t sMask[kStages];
   __shared__ uint32_t sRescale[3];  // by tile mod 3: some head of the tile rescales
   __shared__ int sIdx[TOPK ? kMaxIdx : 1];
@@ -440,7 +538,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   if (tid < 128) {
     sAlpha[tid] = 1.f;
     sAlpha[128 + tid] = 1.f;
-    sL[tid] = 0.f;
   }
 
   // Per-lane LDS bases (element offsets inside a tile).
@@ -613,61 +710,103 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     full_load(ft, Stage<8>{});
   };
 
-  // ---- FP8 tiles: the raw tile is copied global -> LDS (sF) one tile ahead:
-  // 16 loads of 1 KB for the codes (two rows each), 4 for the rotary rows
-  // (eight rows each) and one of 512 B for the scales; wave w issues loads
-  // w, w+4, ... (wave 0 also the scales).  The dequantisation pass then turns
-  // sF into the bf16 tile in its ring slot, 16 codes per thread and unit.
-  auto issue_fp8 = [&](int j) MLA_INLINE {
-    const int pt = p0 + j * kTT;
-    uint32_t base = lds_addr(sF);
-    asm volatile("" : "+s"(base));
+  // ---- FP8 tiles: every wave stages and converts its own part of a tile, so
+  // no barrier separates the staging from the conversion.  Wave w's region of
+  // sF receives, by direct loads one tile ahead of the conversion:
+  //   units u = 0..3 (1 KB each, rows 8u .. 8u+7): lane l's 16 bytes are codes
+  //     16 (l % 8) .. +15 of latent block w of row 8u + l / 8
+  //   scales: 4 bytes per lane l < 32, the block-w scale of row 8 (l % 4) + l / 4
+  //     (so lane l reads the scales of its four rows 8u + l / 8 as one 16 bytes)
+  //   rotary: 16 bytes, chunk l % 8 of rotary row 8 w + l / 8
+  // The conversion writes bf16(float(code) * scale) of lane l's 16 codes per
+  // unit, and the rotary rows, into the tile's ring slot.
+  uint8_t* const fregion = sF + (FP8 ? kFp8Wave * wave : 0);
+  // lane index recomputed at each use: hoisted per-slot addresses would not
+  // fit in the registers the loop leaves
+  auto fresh_lane = [&]() MLA_INLINE -> int {
     int ln = lane;
-    asm volatile("" : "+v"(ln));  // recomputed per tile
-    auto one = [&](auto I) MLA_INLINE {
-      constexpr int i = decltype(I)::value;  // load i = wave + 4k, k < 5 (i < 20)
-      const int li = wave + 4 * i;
-      if (li < 16) {  // codes of rows 2 li + (lane >> 5)
-        const size_t row = seq_row0 + tile_row(pt, 2 * li + (ln >> 5));
-        lds_dma16<0>((const uint8_t*)a.kv + row * kC + (ln & 31) * 16, base + 1024 * li);
-      } else {  // rotary rows 8 (li - 16) + (lane >> 3)
-        const size_t row = seq_row0 + tile_row(pt, 8 * (li - 16) + (ln >> 3));
-        lds_dma16<kFp8Codes + kTT * 16>(a.pe + row * kR + (ln & 7) * 8, base + 1024 * (li - 16));
+    asm volatile("" : "+v"(ln));
+    return ln;
+  };
+  // Load n of a raw tile (issue order, which the conversion's waits count
+  // on): 0 scales, 1..4 code units 0..3, 5 rotary rows.  `dep`: a value read
+  // from the bytes this load replaces (orders the load after that read).
+  // A dense tile of 32 selected rows takes fixed offsets from its first row.
+  auto fp8_load = [&](int j, auto N, uint32_t dep = 0u) MLA_INLINE {
+    constexpr int n = decltype(N)::value;
+    const int pt = p0 + j * kTT;
+    const bool full = !TOPK && pt + kTT <= p1;
+    uint32_t base = lds_addr(fregion);
+    asm volatile("" : "+s"(base));
+    const int ln = fresh_lane();
+    if constexpr (n >= 1 && n <= 4) {
+      constexpr int u = n - 1;
+      const int r = 8 * u + (ln >> 3);
+      const size_t row = seq_row0 + (full ? pt + r : tile_row(pt, r));
+      lds_dma16_after<1024 * u>((const uint8_t*)a.kv + row * kC + kBlk * wave + 16 * (ln & 7), base, dep);
+    } else if constexpr (n == 0) {
+      if (ln < 32) {
+        const int r = 8 * (ln & 3) + (ln >> 2);
+        const size_t row = seq_row0 + (full ? pt + r : tile_row(pt, r));
+        lds_dma4_after<kFp8WaveCodes>(a.kv_scale + row * 4 + wave, base, dep);
       }
-    };
-    one(Stage<0>{});
-    one(Stage<1>{});
-    one(Stage<2>{});
-    one(Stage<3>{});
-    one(Stage<4>{});
-    if (wave == 0 && ln < 32) {  // scales of row `lane`
-      const size_t row = seq_row0 + tile_row(pt, ln);
-      lds_dma16<kFp8Codes>(a.kv_scale + row * 4, base);
+    } else {
+      const int r = 8 * wave + (ln >> 3);
+      const size_t row = seq_row0 + (full ? pt + r : tile_row(pt, r));
+      lds_dma16_after<kFp8WaveCodes + kFp8WaveScales>(a.pe + row * kR + 8 * (ln & 7), base, dep);
     }
   };
-  auto dequant_fp8 = [&](int j, auto S) MLA_INLINE {
+  auto fp8_load_all = [&](int j) MLA_INLINE {
+    fp8_load(j, Stage<0>{});
+    fp8_load(j, Stage<1>{});
+    fp8_load(j, Stage<2>{});
+    fp8_load(j, Stage<3>{});
+    fp8_load(j, Stage<4>{});
+    fp8_load(j, Stage<5>{});
+  };
+  auto fp8_read = [&](auto U) MLA_INLINE -> u32x4 {
+    return *(const u32x4*)(fregion + 1024 * decltype(U)::value + 16 * fresh_lane());
+  };
+  auto fp8_scales = [&]() MLA_INLINE -> f32x4 {  // scales of rows 8u + l / 8, u = 0..3
+    return *(const f32x4*)(fregion + kFp8WaveCodes + 16 * (fresh_lane() >> 3));
+  };
+  // four codes -> two packed bf16 pairs, bf16(float(code) * scale)
+  auto fp8_cvt4 = [&](uint32_t q, float sc) MLA_INLINE -> u32x2 {
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)q, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)q, true);
+    return u32x2{cvt_pk_bf16(lo[0] * sc, lo[1] * sc), cvt_pk_bf16(hi[0] * sc, hi[1] * sc)};
+  };
+  // store half `c` (8 values) of unit u of this lane into the tile
+  auto fp8_store = [&](uint16_t* dst, auto U, int c, const u32x4& w) MLA_INLINE {
+    const int ln = fresh_lane();
+    *(u32x4*)(dst + tile_off(8 * decltype(U)::value + (ln >> 3), 16 * wave + 2 * (ln & 7) + c)) = w;
+  };
+  auto fp8_write = [&](uint16_t* dst, auto U, const u32x4& q, float sc) MLA_INLINE {
+    const u32x2 a = fp8_cvt4(q[0], sc), b = fp8_cvt4(q[1], sc);
+    const u32x2 c = fp8_cvt4(q[2], sc), d = fp8_cvt4(q[3], sc);
+    fp8_store(dst, U, 0, u32x4{a[0], a[1], b[0], b[1]});
+    fp8_store(dst, U, 1, u32x4{c[0], c[1], d[0], d[1]});
+  };
+  auto fp8_rope_read = [&]() MLA_INLINE -> u32x4 {
+    return *(const u32x4*)(fregion + kFp8WaveCodes + kFp8WaveScales + 16 * fresh_lane());
+  };
+  auto fp8_rope_write = [&](uint16_t* dst, const u32x4& v) MLA_INLINE {
+    const int ln = fresh_lane();
+    *(u32x4*)(dst + tile_off(8 * wave + (ln >> 3), 64 + (ln & 7))) = v;
+  };
+  auto fp8_rope = [&](uint16_t* dst) MLA_INLINE { fp8_rope_write(dst, fp8_rope_read()); };
+  // the whole conversion of tile j into slot S in one go (prologue, and waves
+  // without score heads)
+  auto fp8_convert_all = [&](int j, auto S) MLA_INLINE {
     uint16_t* dst = slot(S);
-    const float* scl = (const float*)(sF + kFp8Codes);
-    int th = tid;
-    asm volatile("" : "+v"(th));  // addresses recomputed per tile, not kept live per slot
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int u = th + kAttnThreads * k, t = u >> 5, cc = u & 31;
-      const u32x4 q = *(const u32x4*)(sF + t * kC + cc * 16);
-      const float sc = scl[t * 4 + (cc >> 3)];
-      uint32_t w[8];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[d], false);
-        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)q[d], true);
-        w[2 * d] = cvt_pk_bf16(lo[0] * sc, lo[1] * sc);
-        w[2 * d + 1] = cvt_pk_bf16(hi[0] * sc, hi[1] * sc);
-      }
-      *(u32x4*)(dst + tile_off(t, 2 * cc)) = u32x4{w[0], w[1], w[2], w[3]};
-      *(u32x4*)(dst + tile_off(t, 2 * cc + 1)) = u32x4{w[4], w[5], w[6], w[7]};
-    }
-    const u32x4 pv = *(const u32x4*)(sF + kFp8Codes + kTT * 16 + th * 16);
-    *(u32x4*)(dst + tile_off(th >> 3, 64 + (th & 7))) = pv;
+    const f32x4 sc = fp8_scales();
+    const u32x4 q0 = fp8_read(Stage<0>{}), q1 = fp8_read(Stage<1>{});
+    const u32x4 q2 = fp8_read(Stage<2>{}), q3 = fp8_read(Stage<3>{});
+    fp8_write(dst, Stage<0>{}, q0, sc[0]);
+    fp8_write(dst, Stage<1>{}, q1, sc[1]);
+    fp8_write(dst, Stage<2>{}, q2, sc[2]);
+    fp8_write(dst, Stage<3>{}, q3, sc[3]);
+    fp8_rope(dst);
     publish_mask(p0 + j * kTT, decltype(S)::value);
   };
 
@@ -685,21 +824,21 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   // ---- pipeline prologue: the first tiles and the query are loaded
   // together, and everything is complete before the loop
   if (!FP8) issue_bf16(0, Stage<0>{});
-  else issue_fp8(0);
+  else fp8_load_all(0);
   // Absorbed query + q_pe of this lane's head: k-step s covers elements
-  // 16s..16s+15, lane group g holds 8 of them.
+  // 16s..16s+15, lane group g holds 8 of them (stored in this order by the
+  // absorb kernel: one 1 KB row per wave and k-step).
   u32x4 qreg[36];
   if (active) {
-    const u32x4* src = (const u32x4*)(a.qt + ((size_t)b * a.Hp + head) * kQK);
+    const u32x4* src = (const u32x4*)(a.qt + ((size_t)b * a.head_blocks + wave) * (36 * 512)) + lane;
 #pragma unroll
-    for (int st = 0; st < 36; ++st) qreg[st] = src[2 * st + g];
+    for (int st = 0; st < 36; ++st) qreg[st] = src[64 * st];
   }
   MLA_WAIT_VMCNT(0);
-  if (FP8) {  // tile 0 into slot 0, then the raw tile 1 on its way
-    MLA_LDS_BARRIER();
-    dequant_fp8(0, Stage<0>{});
-    MLA_LDS_BARRIER();
-    if (1 < ntiles) issue_fp8(1);
+  if (FP8) {  // this wave's part of tile 0 into slot 0, then the raw tile 1 on its way
+    fp8_convert_all(0, Stage<0>{});
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staging reads done before the reload
+    if (1 < ntiles) fp8_load_all(1);
   }
 
   // ---- software pipeline over the tiles, one workgroup barrier per tile.
@@ -883,28 +1022,26 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     // own loads of it); P, alpha and flag of tile j-1 visible; every wave is
     // done with tile j-2 and with the P buffer and flag the softmax of tile j
     // is about to write.
-    MLA_WAIT_VMCNT(0);
+    if (!FP8) MLA_WAIT_VMCNT(0);
     MLA_LDS_BARRIER();
     // tile j+1: a full dense tile is loaded by the fast path, its nine loads
     // per thread spread over the score MFMAs; any other tile in one burst here.
-    // FP8: the raw tile j+1 (staged during tile j-1) is dequantised into its
-    // slot, then a second barrier frees the staging buffer for tile j+2.
+    // FP8: this wave's part of tile j+1 (staged during tile j-1) is converted
+    // into its slot during the score MFMAs, then the raw tile j+2 is loaded
+    // into the staging region (its own reads of it done).
     const bool fast = !FP8 && !TOPK && j + 1 < ntiles && p0 + (j + 2) * kTT <= p1;
+    const bool fp8_cv = FP8 && j + 1 < ntiles, fp8_ld = FP8 && j + 2 < ntiles;
     const FullTile ft = full_tile(j + 1, Stage<s1>{});
-    if (j + 1 < ntiles) {
-      if (FP8) {
-        dequant_fp8(j + 1, Stage<s1>{});
-        MLA_LDS_BARRIER();
-        if (j + 2 < ntiles) issue_fp8(j + 2);
-      } else if (fast) {
-        publish_mask(p0 + (j + 1) * kTT, s1);
-      } else {
-        issue_bf16(j + 1, Stage<s1>{});
-      }
+    if (!FP8 && j + 1 < ntiles) {
+      if (fast) publish_mask(p0 + (j + 1) * kTT, s1);
+      else issue_bf16(j + 1, Stage<s1>{});
     }
     if (tid == 0) sRescale[(j + 1) % 3] = 0u;  // flag of tile j-2: read in body j-1
     const uint16_t* tile = slot(S);
     f32x16 s = {};  // waves without score heads run the softmax on zeros
+    u32x4 fq;       // FP8: staged codes of one unit
+    u32x2 fw;       // and the first bf16 pair of the half being converted
+    f32x4 fsc = {};  // and the scales of its four rows
     if (active) {
       // Scores.  The 36 MFMAs accumulate in VGPRs (inline asm: the compiler
       // would put this accumulator in AGPRs, where O already takes all 256).
@@ -931,6 +1068,53 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
         if constexpr (kk == 1) {
           if (fast) full_load(ft, Q);
         }
+        if constexpr (FP8) {
+          // conversion of tile j+1, one dword of codes per MFMA (the VALU work
+          // fits beside the MFMA): unit u is read at step 8u, converted at
+          // steps 8u+2 .. 8u+5, and its staging bytes are reloaded with tile
+          // j+2 once read (scales at step 2, unit u at 8u+3, rotary at 32), so
+          // each load has about one tile of time to land.  Waits count loads
+          // in issue order: tile j+1's later loads, then tile j+2's issued ones.
+          if constexpr (k % 8 == 0 && k < 32) {
+            if (fp8_cv) {
+              constexpr int u = k / 8;
+              if (u > 0 && fp8_ld) MLA_WAIT_VMCNT(5);
+              else MLA_WAIT_VMCNT(4 - u);  // scales (first load) and unit u
+              if constexpr (u == 0) fsc = fp8_scales();
+              fq = fp8_read(Stage<u>{});
+            }
+          }
+          if constexpr (k % 8 >= 2 && k % 8 <= 5 && k < 32) {
+            if (fp8_cv) {
+              constexpr int u = k / 8, d = k % 8 - 2;
+              const u32x2 w = fp8_cvt4(fq[d], fsc[u]);
+              if constexpr (d & 1) fp8_store(slot(Stage<s1>{}), Stage<u>{}, d >> 1, u32x4{fw[0], fw[1], w[0], w[1]});
+              else fw = w;
+            }
+            if constexpr (k == 2) {
+              if (fp8_ld) fp8_load(j + 2, Stage<0>{}, __float_as_uint(fsc[0]));
+            }
+            if constexpr (k % 8 == 3) {
+              if (fp8_ld) fp8_load(j + 2, Stage<k / 8 + 1>{}, fq[0]);
+            }
+          }
+          if constexpr (k == 30) {
+            if (fp8_cv) {
+              if (fp8_ld) MLA_WAIT_VMCNT(5);
+              else MLA_WAIT_VMCNT(0);
+              fq = fp8_rope_read();
+            }
+          }
+          if constexpr (k == 31) {
+            if (fp8_cv) {
+              fp8_rope_write(slot(Stage<s1>{}), fq);
+              publish_mask(p0 + (j + 1) * kTT, s1);
+            }
+          }
+          if constexpr (k == 32) {
+            if (fp8_ld) fp8_load(j + 2, Stage<5>{}, fq[0]);
+          }
+        }
         if constexpr (k == 35) asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s));
       };
       auto group = [&](auto Q) MLA_INLINE {
@@ -950,6 +1134,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
       group(Stage<8>{});
     } else if (fast) {
       full_all(ft);
+    } else if (FP8) {
+      if (fp8_cv) {
+        MLA_WAIT_VMCNT(0);
+        fp8_convert_all(j + 1, Stage<s1>{});
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      if (fp8_ld) fp8_load_all(j + 2);
     }
     const uint32_t mask = sMask[st];
     // one code path for every wave inside the loop (branches around the
@@ -974,132 +1165,139 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     update_only(lt, jl);
   }
 
-  // ---- partial result: (m, l) in fp32 and O / l in bf16,
-  // staged through the idle ring (head blocks 0-2 in slots 0-2, then block 3
-  // in slot 0; rows of kOStride) so that every head's 512 values leave as one
-  // 1 KB row.
+  // ---- partial result: (m, l) in fp32 and the unnormalised O in bf16, each
+  // lane's accumulators stored in fragment order:
+  //   part_o[slot][head block nb][wave][m][q2][lane][8]
+  // holds O[head 32 nb + lane % 32][128 wave + 32 m + 16 q2 + 8 (j / 4)
+  // + 4 (lane / 32) + j % 4] at position j, one 1 KB row per store.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (active && g == 0) {
-    sL[head] = l_tot;
-    if (head < a.H) {
-      float* pm = a.part_ml + (slot_id * a.H + head) * 2;
-      pm[0] = l_tot > 0.f ? m_run : -INFINITY;
-      pm[1] = l_tot;
-    }
+  if (active && g == 0 && head < a.H) {
+    float* pm = a.part_ml + (slot_id * a.H + head) * 2;
+    pm[0] = l_tot > 0.f ? m_run : -INFINITY;
+    pm[1] = l_tot;
   }
-  __syncthreads();  // ring idle, sL complete
-  auto stage_out = [&](auto NB, auto SL) MLA_INLINE {
+  uint16_t* dst = a.part_o + slot_id * (size_t)a.Hp * kC + (size_t)wave * (8 * 512) + 8 * lane;
+  auto store_block = [&](auto NB) MLA_INLINE {
     constexpr int nb = decltype(NB)::value;
-    const float lt = sL[32 * nb + n];
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    uint16_t* row = slot(SL) + n * kOStride + 128 * wave + 4 * g;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const f32x16& ob = o[4 * m + nb];
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *(u32x2*)(row + 32 * m + 8 * q) =
-            u32x2{cvt_pk_bf16(ob[4 * q] * inv, ob[4 * q + 1] * inv), cvt_pk_bf16(ob[4 * q + 2] * inv, ob[4 * q + 3] * inv)};
+      for (int q2 = 0; q2 < 2; ++q2)
+        *(u32x4*)(dst + (size_t)nb * (32 * 512) + (2 * m + q2) * 512) =
+            u32x4{cvt_pk_bf16(ob[8 * q2], ob[8 * q2 + 1]), cvt_pk_bf16(ob[8 * q2 + 2], ob[8 * q2 + 3]),
+                  cvt_pk_bf16(ob[8 * q2 + 4], ob[8 * q2 + 5]), cvt_pk_bf16(ob[8 * q2 + 6], ob[8 * q2 + 7])};
     }
   };
-  stage_out(Stage<0>{}, Stage<0>{});
-  stage_out(Stage<1>{}, Stage<1>{});
-  stage_out(Stage<2>{}, Stage<2>{});
-  __syncthreads();
-  uint16_t* dst = a.part_o + slot_id * a.H * kC;
-  auto copy_out = [&](auto NB, auto SL) MLA_INLINE {
-    constexpr int nb = decltype(NB)::value;
-    const uint16_t* srcb = slot(SL);
-#pragma unroll 2
-    for (int i = tid; i < 32 * 64; i += kAttnThreads) {
-      const int h = 32 * nb + (i >> 6), c16 = i & 63;
-      if (h < a.H) *(u32x4*)(dst + (size_t)h * kC + 8 * c16) = *(const u32x4*)(srcb + (i >> 6) * kOStride + 8 * c16);
-    }
-  };
-  copy_out(Stage<0>{}, Stage<0>{});
-  copy_out(Stage<1>{}, Stage<1>{});
-  copy_out(Stage<2>{}, Stage<2>{});
-  if (a.H > 96) {  // head block 3 through slot 0 (uniform branch)
-    __syncthreads();
-    stage_out(Stage<3>{}, Stage<0>{});
-    __syncthreads();
-    copy_out(Stage<3>{}, Stage<0>{});
-  }
+  store_block(Stage<0>{});
+  if (a.head_blocks > 1) store_block(Stage<1>{});
+  if (a.head_blocks > 2) store_block(Stage<2>{});
+  if (a.head_blocks > 3) store_block(Stage<3>{});
 }
 
 // ---------------------------------------------------------------------------
-// combine: grid (H, B, 2 column halves), 256 threads.  Sequence b's partials
-// sit in slots wcum[b] .. wcum[b+1]-1, one per attention workgroup of b.
-// Thread (sg = tid/32, co = tid%32) accumulates 8 columns over the partials
-// s = sg, sg+8, ...; the eight groups are added through LDS.
-//   M = max_s m_s,  w_s = l_s 2^(m_s - M),  o = sum_s w_s O_s / sum_s w_s
+// combine: grid (B, head_blocks * 32 partial rows), 64 x NG threads (NG =
+// 1, 2, 4 or 8 groups, about one per four partials a sequence has on
+// average).  Row r of a partial is (head block r / 32, wave, m, q2) in the
+// attention kernel's fragment order: 64 lanes x 8 values, lane l holding head
+// 32 (r / 32) + l % 32.  Thread (lane, group sg) merges that chunk over every
+// NG-th partial of sequence b (slots wcum[b] .. wcum[b+1] - 1) with a running
+// maximum, the groups are merged through LDS, and
+//   o = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j,  M = max_j m_j
+// (over the partials with l_j > 0; none: zeros) goes to olat[b][h][c].
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ part_o,
-                                                      const float* __restrict__ part_ml,
-                                                      const int32_t* __restrict__ wcum,
-                                                      uint16_t* __restrict__ olat, int H) {
-  const int h = blockIdx.x, b = blockIdx.y, half = blockIdx.z, tid = threadIdx.x;
-  const int sg = tid >> 5, co = tid & 31;
+constexpr int kCombineGroups = 8;
+
+struct Merge {
+  float M = -INFINITY, L = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  // add weight 2^m times the partial (values v[e] * scale, sum l)
+  __device__ __forceinline__ void add(float m, float l, const float* v) {
+    if (!(l > 0.f)) return;  // nothing selected in that split
+    if (m > M) {
+      const float sc = exp2f(M - m);  // M = -inf: 0
+      L *= sc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= sc;
+      M = m;
+    }
+    const float w = exp2f(m - M);
+    L = fmaf(w, l, L);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, v[e], acc[e]);
+  }
+};
+
+__global__ __launch_bounds__(64 * kCombineGroups) void combine_kernel(
+    const uint16_t* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ wcum, uint16_t* __restrict__ olat, int H, int Hp) {
+  const int NG = blockDim.x >> 6;
+  const int b = blockIdx.x, r = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, sg = tid >> 6;
+  const int h = 32 * (r >> 5) + (lane & 31);
+  const bool hv = h < H;
   const size_t s0 = (size_t)wcum[b];
   const int ns = wcum[b + 1] - wcum[b];
-  const size_t bh = (size_t)b * H + h;
-  const float* pm = part_ml + (s0 * H + h) * 2;
-  const uint16_t* po = part_o + (s0 * H + h) * kC + 256 * half + 8 * co;
-  const size_t ml_stride = (size_t)H * 2, o_stride = (size_t)H * kC;
-  // M: each lane of the wave reads every 64th partial's (m, l), then a wave max
-  float M = -INFINITY;
-  for (int s = tid & 63; s < ns; s += 64) {
-    const float2 ml = *(const float2*)(pm + s * ml_stride);
-    if (ml.y > 0.f) M = fmaxf(M, ml.x);
-  }
-  M = wave_max(M);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  int s = sg;
-  for (; s + 24 < ns; s += 32) {  // four partials of this group in flight
-    u32x4 v[4];
-    float w[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float2 ml = *(const float2*)(pm + (s + 8 * k) * ml_stride);
-      w[k] = ml.y > 0.f ? ml.y * exp2f(ml.x - M) : 0.f;
-      v[k] = *(const u32x4*)(po + (size_t)(s + 8 * k) * o_stride);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      L += w[k];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        acc[2 * j] = fmaf(w[k], bf_lo(v[k][j]), acc[2 * j]);
-        acc[2 * j + 1] = fmaf(w[k], bf_hi(v[k][j]), acc[2 * j + 1]);
-      }
-    }
-  }
-  for (; s < ns; s += 8) {
-    const float2 ml = *(const float2*)(pm + s * ml_stride);
-    const float w = ml.y > 0.f ? ml.y * exp2f(ml.x - M) : 0.f;
-    const u32x4 v = *(const u32x4*)(po + (size_t)s * o_stride);
-    L += w;
+  const float* pm = part_ml + (s0 * H + (hv ? h : 0)) * 2;
+  const uint16_t* po = part_o + s0 * Hp * kC + (size_t)r * 512 + 8 * lane;
+  const size_t ml_stride = (size_t)H * 2, o_stride = (size_t)Hp * kC;
+  __shared__ float sRed[kCombineGroups - 1][64][10];
+  Merge mg;
+  auto unpack = [](const u32x4& v, float* f) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      acc[2 * j] = fmaf(w, bf_lo(v[j]), acc[2 * j]);
-      acc[2 * j + 1] = fmaf(w, bf_hi(v[j]), acc[2 * j + 1]);
+      f[2 * j] = bf_lo(v[j]);
+      f[2 * j + 1] = bf_hi(v[j]);
+    }
+  };
+  if (hv) {
+    int s = sg;
+    for (; s + 3 * NG < ns; s += 4 * NG) {  // four partials of this group in flight
+      u32x4 v[4];
+      float2 ml[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        ml[k] = *(const float2*)(pm + (s + NG * k) * ml_stride);
+        v[k] = *(const u32x4*)(po + (size_t)(s + NG * k) * o_stride);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        float f[8];
+        unpack(v[k], f);
+        mg.add(ml[k].x, ml[k].y, f);
+      }
+    }
+    for (; s < ns; s += NG) {
+      const float2 ml = *(const float2*)(pm + s * ml_stride);
+      const u32x4 v = *(const u32x4*)(po + (size_t)s * o_stride);
+      float f[8];
+      unpack(v, f);
+      mg.add(ml.x, ml.y, f);
     }
   }
-  __shared__ float red[8][256 + 4];
-  __shared__ float lred[8];
+  if (sg > 0) {
+    float* d = sRed[sg - 1][lane];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) red[sg][8 * co + e] = acc[e];
-  if (co == 0) lred[sg] = L;
-  __syncthreads();
-  float o = 0.f, Lt = 0.f;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    o += red[k][tid];
-    Lt += lred[k];
+    for (int e = 0; e < 8; ++e) d[e] = mg.acc[e];
+    d[8] = mg.M;
+    d[9] = mg.L;
   }
-  const float inv = Lt > 0.f ? 1.f / Lt : 0.f;
-  olat[bh * kC + 256 * half + tid] = (uint16_t)f2bf(o * inv);
+  __syncthreads();
+  if (sg == 0 && hv) {
+    for (int k = 0; k < NG - 1; ++k) {
+      const float* d = sRed[k][lane];
+      // a group's (acc, L) is already relative to 2^M_k: merge as a partial
+      // with m = M_k, l = L_k and values acc_k / 1
+      mg.add(d[8], d[9], d);
+    }
+    const float inv = mg.L > 0.f ? 1.f / mg.L : 0.f;
+    // row r = (head block, wave, m, q2): columns 128 wave + 32 m + 16 q2 + 4 (lane / 32)
+    const int c0 = 128 * ((r >> 3) & 3) + 32 * ((r >> 1) & 3) + 16 * (r & 1) + 4 * (lane >> 5);
+    uint16_t* dst = olat + ((size_t)b * H + h) * kC + c0;
+    const float* a = mg.acc;
+    *(u32x2*)dst = u32x2{pack_bf(a[0] * inv, a[1] * inv), pack_bf(a[2] * inv, a[3] * inv)};
+    *(u32x2*)(dst + 8) = u32x2{pack_bf(a[4] * inv, a[5] * inv), pack_bf(a[6] * inv, a[7] * inv)};
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1174,9 +1372,12 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
     write_cols = (int)std::min<long long>((items + items_per_col - 1) / items_per_col, 64);
     absorb = fp8 ? absorb_kernel<kWriteFp8> : absorb_kernel<kWriteBf16>;
   }
-  err = launch_kernel(absorb, dim3(plan.heads_padded + 1 + write_cols, 4), dim3(256), stream,
-                      evk(0), (const uint16_t*)d.q_nope, (const uint16_t*)d.q_pe,
-                      (const uint16_t*)d.wkv_b, qt, B, H, plan.heads_padded, d.cache_lens,
+  // sequences per absorb workgroup: blocks of 32, over at most 8 ranges
+  const int chunks = (B + 31) / 32, zs = std::min(chunks, 8);
+  const int bz = 32 * ((chunks + zs - 1) / zs);
+  err = launch_kernel(absorb, dim3(plan.heads_padded + 1 + write_cols, 4, (B + bz - 1) / bz),
+                      dim3(256), stream, evk(0), (const uint16_t*)d.q_nope, (const uint16_t*)d.q_pe,
+                      (const uint16_t*)d.wkv_b, qt, B, H, plan.heads_padded, bz, d.cache_lens,
                       p.max_seq_len, p.topk, plan.min_group_tiles, (int)plan.max_groups, wcum, rec,
                       rw);
   if (err != hipSuccess) return err;
@@ -1203,8 +1404,13 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
   err = launch_kernel(attn, agrid, dim3(kAttnThreads), stream, evk(1), aa);
   if (err != hipSuccess) return err;
 
-  err = launch_kernel(combine_kernel, dim3(H, B, 2), dim3(256), stream, evk(2),
-                      (const uint16_t*)part_o, (const float*)part_ml, (const int32_t*)wcum, olat, H);
+  // partial groups per combine thread block: about one per 4 partials of the
+  // average sequence (at most 256 partials are in use when B <= 256)
+  const long long avg_parts = std::max<long long>(1, std::min<long long>(plan.max_groups, 256) / B);
+  const int ng = avg_parts >= 32 ? 8 : (avg_parts >= 16 ? 4 : (avg_parts >= 8 ? 2 : 1));
+  err = launch_kernel(combine_kernel, dim3(B, plan.head_blocks * 32), dim3(64 * ng), stream, evk(2),
+                      (const uint16_t*)part_o, (const float*)part_ml, (const int32_t*)wcum, olat, H,
+                      plan.heads_padded);
   if (err != hipSuccess) return err;
 
   err = launch_kernel(uproj_kernel, dim3(H, 4), dim3(64), stream, evk(3), (const uint16_t*)olat,

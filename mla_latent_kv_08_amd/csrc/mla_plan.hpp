@@ -52,10 +52,10 @@ inline DecodePlan make_decode_plan(const mla_params& p) {
   }
   d.max_groups = G;
   size_t off = 0;
-  d.off_qt = off;  // bf16 [B][heads_padded][576]
+  d.off_qt = off;  // bf16 [B][heads_padded][576], in the attention kernel's fragment order
   off = align256(off + (size_t)B * d.heads_padded * 576 * 2);
-  d.off_part_o = off;  // bf16 [max_groups][H][512]
-  off = align256(off + (size_t)G * H * 512 * 2);
+  d.off_part_o = off;  // bf16 [max_groups][heads_padded][512], in fragment order
+  off = align256(off + (size_t)G * d.heads_padded * 512 * 2);
   d.off_part_ml = off;  // fp32 [max_groups][H][2]
   off = align256(off + (size_t)G * H * 2 * 4);
   d.off_olat = off;  // bf16 [B][H][512]
