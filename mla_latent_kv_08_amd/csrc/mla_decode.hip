@@ -86,12 +86,32 @@ __device__ long long block_sum_256(long long v, long long* red) {
 
 constexpr int kPlanCache = 2048;  // per-sequence values kept in LDS by the planner
 
+constexpr int kXcds = 8;  // MI355X: accelerator complex dies, each with its own L2
+
+// Attention workgroup i runs on XCD i % 8 (round-robin dispatch).  Of the n
+// workgroups in use, XCD x (workgroups x, x + 8, ...) takes the plan slots
+// [x q + min(x, r), ...) in order, q = n / 8, r = n % 8, so the workgroups of
+// one sequence share an L2 and fetch its absorbed query there once.  This is
+// the workgroup that runs plan slot s.
+__device__ __forceinline__ int xcd_workgroup(int s, int n) {
+  const int q = n / kXcds, r = n % kXcds, big = r * (q + 1);
+  int x, k;
+  if (s < big) {
+    x = s / (q + 1);
+    k = s - x * (q + 1);
+  } else {
+    x = r + (s - big) / q;
+    k = (s - big) - (x - r) * q;
+  }
+  return x + kXcds * k;
+}
+
 // Work plan of one decode call, computed by one workgroup of 256 threads (the
 // split is described with make_decode_plan): picks the tile budget S, then
 // writes wcum[b] = k_0 + ... + k_{b-1} (wcum[B] = workgroups in use) and, for
 // each of the G attention workgroups, the record {sequence, first tile, end
-// tile, clamped length} (sequence -1: workgroup unused), so that a workgroup
-// starts from one 16-byte load.
+// tile, clamped length} (sequence -1: workgroup unused) and the plan slot its
+// partial goes to, so that a workgroup starts from two independent loads.
 // floor(a / b) and ceil(a / b) for 0 <= a < 2^52 and b >= 1.  Both are
 // exact in double, and a non-integer quotient a/b lies at least 1/b from the
 // nearest integer n, more than half an ulp of n (n * 2^-53 < 1/b because
@@ -109,7 +129,7 @@ __device__ __forceinline__ long long ceil_div(long long a, long long b) {
 constexpr int kPlanLdsBytes = 12 * 8 + 4 * 4 + (3 * kPlanCache + 1) * 4 + 32 * 4;
 
 __device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min_tiles, int G,
-                            int32_t* wcum, int4* rec, char* lds) {
+                            int32_t* wcum, int4* rec, int32_t* slot_of, char* lds) {
   long long* red = (long long*)lds;           // [12]
   int* sc = (int*)(lds + 96);                 // [4]
   int* tl = sc + 4;                           // [kPlanCache] tiles of sequence b
@@ -185,6 +205,15 @@ __device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min
   }
   if (S < min_tiles) S = min_tiles;
   if (topk > 0 && S > kMaxTopkGroupTiles) S = kMaxTopkGroupTiles;
+  // workgroups in use (records are placed by xcd_workgroup over this count)
+  long long cnt = 0;
+  for (int bb = tid; bb < B; bb += 256) cnt += ceil_div(tiles(bb), S);
+  const int used = (int)block_sum_256(cnt, red);
+  auto put = [&](int slot, int4 r) {
+    const int i = xcd_workgroup(slot, used);
+    rec[i] = r;
+    slot_of[i] = slot;
+  };
   int run = 0, total;
   for (int base = 0; base < B; base += 256) {
     const int bb = base + tid;
@@ -196,8 +225,8 @@ __device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min
       if (bb >= kPlanCache) {  // long batches: these records come from the sequence's own thread
         const int t = tiles_of(bb), len = seq_len(lens, bb, T);
         for (int p = 0; p < k; ++p)
-          rec[run + incl - k + p] =
-              make_int4(bb, (int)floor_div((long long)p * t, k), (int)floor_div((long long)(p + 1) * t, k), len);
+          put(run + incl - k + p,
+              make_int4(bb, (int)floor_div((long long)p * t, k), (int)floor_div((long long)(p + 1) * t, k), len));
       }
     }
     run += total;
@@ -221,9 +250,9 @@ __device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min
       else hi = mid - 1;
     }
     const int t = tl[lo], k = sw[lo + 1] - sw[lo], p = i - sw[lo];
-    rec[i] = make_int4(lo, (int)floor_div((long long)p * t, k), (int)floor_div((long long)(p + 1) * t, k), sl[lo]);
+    put(i, make_int4(lo, (int)floor_div((long long)p * t, k), (int)floor_div((long long)(p + 1) * t, k), sl[lo]));
   }
-  for (int i = run + tid; i < G; i += 256) rec[i] = make_int4(-1, 0, 0, 0);
+  for (int i = used + tid; i < G; i += 256) rec[i] = make_int4(-1, 0, 0, 0);
 }
 
 enum RowWriteMode { kNoWrite = 0, kWriteBf16 = 1, kWriteFp8 = 2 };
@@ -286,7 +315,8 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
                                                      uint16_t* __restrict__ qt, int B, int H,
                                                      int Hp, int bz, const int32_t* __restrict__ lens,
                                                      int T, int topk, int min_group_tiles,
-                                                     int G, int32_t* wcum, int4* rec, RowWrite rw) {
+                                                     int G, int32_t* wcum, int4* rec,
+                                                     int32_t* slot_of, RowWrite rw) {
   // one LDS buffer: the planner's arrays, or the W_UK tile, whose space the
   // output tile reuses once the fragments are in registers
   constexpr int kWRow = 128 + 8;  // padded tile rows (bf16)
@@ -296,7 +326,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
   if (h >= Hp) {
     if (blockIdx.z != 0) return;
     if (h == Hp) {
-      if (cblk == 0) plan_groups(lens, B, T, topk, min_group_tiles, G, wcum, rec, smem);
+      if (cblk == 0) plan_groups(lens, B, T, topk, min_group_tiles, G, wcum, rec, slot_of, smem);
     } else if (WRITE != kNoWrite) {
       write_new_rows<WRITE>(rw, lens, B, T, (h - Hp - 1) * 4 + cblk, (gridDim.x - Hp - 1) * 4);
     }
@@ -425,6 +455,7 @@ struct AttnArgs {
   const uint16_t* pe;
   const int32_t* topk_idx;
   const int4* rec;        // [grid] {sequence or -1, first tile, end tile, length}
+  const int32_t* slot_of; // [grid] plan slot (partial index) of each workgroup
   uint16_t* part_o;       // [grid][H][512]
   float* part_ml;         // [grid][H][2]
   int B, H, Hp, T, topk, head_blocks;
@@ -500,13 +531,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int4 rec = a.rec[grp];
+  const int part_slot = a.slot_of[grp];
   if (rec.x < 0) return;  // whole workgroup: not used by the plan
   const int b = rec.x, t_lo = rec.y, t_hi = rec.z, len = rec.w;
   const int n_b = TOPK ? (len > 0 ? a.topk : 0) : len;
   const int p0 = t_lo * kTT, p1 = min(t_hi * kTT, n_b);
   const int ntiles = t_hi - t_lo;
   const size_t seq_row0 = (size_t)b * a.T;
-  const size_t slot_id = grp;
+  const size_t slot_id = part_slot;
 
   // One LDS array per ring slot (not one 2-D array): the slot a tile lives in
   // is a compile-time constant in the loop body below.
@@ -1359,6 +1391,7 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
   hipError_t err;
   int32_t* wcum = (int32_t*)(ws + plan.off_wcum);
   int4* rec = (int4*)(ws + plan.off_rec);
+  int32_t* slot_of = (int32_t*)(ws + plan.off_slot);
 
   const bool fp8 = p.kv_dtype == MLA_KV_FP8_E4M3_B128, topk = p.topk > 0;
   RowWrite rw{};
@@ -1379,7 +1412,7 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
                       dim3(256), stream, evk(0), (const uint16_t*)d.q_nope, (const uint16_t*)d.q_pe,
                       (const uint16_t*)d.wkv_b, qt, B, H, plan.heads_padded, bz, d.cache_lens,
                       p.max_seq_len, p.topk, plan.min_group_tiles, (int)plan.max_groups, wcum, rec,
-                      rw);
+                      slot_of, rw);
   if (err != hipSuccess) return err;
 
   AttnArgs aa;
@@ -1389,6 +1422,7 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
   aa.pe = (const uint16_t*)d.pe_cache;
   aa.topk_idx = d.topk_idx;
   aa.rec = rec;
+  aa.slot_of = slot_of;
   aa.part_o = part_o;
   aa.part_ml = part_ml;
   aa.B = B;

@@ -32,7 +32,7 @@ struct DecodePlan {
   long long max_groups; // attention grid (upper bound of sum k_b)
   int min_group_tiles;  // lower bound of S
   long long max_tiles;  // tiles of the longest possible selection
-  size_t off_qt, off_part_o, off_part_ml, off_olat, off_wcum, off_rec, bytes;
+  size_t off_qt, off_part_o, off_part_ml, off_olat, off_wcum, off_rec, off_slot, bytes;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -64,6 +64,8 @@ inline DecodePlan make_decode_plan(const mla_params& p) {
   off = align256(off + ((size_t)B + 1) * 4);
   d.off_rec = off;  // int32 [max_groups][4]: sequence (-1: unused), first tile, end tile, length
   off = align256(off + (size_t)G * 16);
+  d.off_slot = off;  // int32 [max_groups]: plan slot (partial index) run by each workgroup
+  off = align256(off + (size_t)G * 4);
   d.bytes = off;
   return d;
 }
