@@ -32,6 +32,11 @@
  *    codes 0.
  *  - The decode sees the latent the page's cache holds: bf16(code * scale).
  *  - Per-sequence end: end_b = min(max(cache_lens[b], 0), max_seq_len).
+ *  - s > 1 query tokens: they are the last s cached positions of the
+ *    sequence, and token i (0-based) sees the rows up to its own,
+ *    t < end_b - (s - 1 - i) (the MQA decode excerpt carries the s dimension
+ *    in its einsums but prints its mask for one token only).  With top-k,
+ *    token i has its own index row topk_idx[b][i].
  *  - Top-k: the selected positions are the SET of entries i of topk_idx[b]
  *    with 0 <= i < end_b (the page's scatter of 0 into a -inf mask is
  *    idempotent, so duplicates count once; order is irrelevant).
@@ -197,19 +202,23 @@ static double latent_at(int fp8, const void* kv_cache, const float* kv_scale, si
 /* Decode (page "KV cache", MQA decode excerpt; MLA article, s.3-4)    */
 /* ------------------------------------------------------------------ */
 
-/* One (sequence b, head h) output row out[128]; optionally the softmax
- * probabilities over positions 0..max_seq_len-1 (0 where not selected). */
-static void decode_one(const oracle_decode_args* a, int b, int h, double* out, double* probs) {
+/* One (query token q = b * s + i, head h) output row out[128]; optionally
+ * the softmax probabilities over positions 0..max_seq_len-1 (0 where not
+ * selected). */
+static void decode_one(const oracle_decode_args* a, int q, int h, double* out, double* probs) {
   const int T = a->max_seq_len;
+  const int b = q / a->s, i_tok = q % a->s;
   int end = a->cache_lens[b];
   if (end < 0) end = 0;
   if (end > T) end = T;
+  end -= a->s - 1 - i_tok; /* rows up to this token's own */
+  if (end < 0) end = 0;
 
   /* Selected positions. */
   unsigned char* sel = (unsigned char*)calloc((size_t)T, 1);
   if (a->topk > 0) {
     for (int i = 0; i < a->topk; ++i) {
-      int32_t t = a->topk_idx[(size_t)b * a->topk + i];
+      int32_t t = a->topk_idx[(size_t)q * a->topk + i];
       if (t >= 0 && t < end) sel[t] = 1;
     }
   } else {
@@ -221,9 +230,9 @@ static void decode_one(const oracle_decode_args* a, int b, int h, double* out, d
   for (int c = 0; c < ORC_C; ++c) {
     double acc = 0.0;
     for (int d = 0; d < ORC_DN; ++d) {
-      double q = oracle_bf16_value(a->q_nope[((size_t)b * a->H + h) * ORC_DN + d]);
+      double qn = oracle_bf16_value(a->q_nope[((size_t)q * a->H + h) * ORC_DN + d]);
       double w = oracle_bf16_value(a->wkv_b[((size_t)h * (ORC_DN + ORC_DV) + d) * ORC_C + c]);
-      acc += q * w;
+      acc += qn * w;
     }
     qa[c] = acc;
   }
@@ -238,7 +247,7 @@ static void decode_one(const oracle_decode_args* a, int b, int h, double* out, d
     for (int c = 0; c < ORC_C; ++c) content += qa[c] * latent_at(a->fp8, a->kv_cache, a->kv_scale, row, c);
     double rope = 0.0;
     for (int r = 0; r < ORC_R; ++r) {
-      double qp = oracle_bf16_value(a->q_pe[((size_t)b * a->H + h) * ORC_R + r]);
+      double qp = oracle_bf16_value(a->q_pe[((size_t)q * a->H + h) * ORC_R + r]);
       double kr = oracle_bf16_value(a->pe_cache[row * ORC_R + r]);
       rope += qp * kr;
     }
@@ -282,15 +291,15 @@ static void decode_one(const oracle_decode_args* a, int b, int h, double* out, d
 
 int oracle_decode(const oracle_decode_args* a, int n_pairs, const int32_t* pairs, double* out,
                   double* probs) {
-  if (!a || a->B < 0 || a->H <= 0 || a->max_seq_len <= 0 || a->topk < 0) return 1;
+  if (!a || a->B < 0 || a->H <= 0 || a->max_seq_len <= 0 || a->topk < 0 || a->s < 1) return 1;
   if (a->topk > 0 && !a->topk_idx) return 1;
   if (a->fp8 && !a->kv_scale) return 1;
-  int n = pairs ? n_pairs : a->B * a->H;
+  int n = pairs ? n_pairs : a->B * a->s * a->H;
 #pragma omp parallel for schedule(dynamic, 1)
   for (int i = 0; i < n; ++i) {
-    int b = pairs ? pairs[2 * i] : i / a->H;
+    int q = pairs ? pairs[2 * i] : i / a->H;
     int h = pairs ? pairs[2 * i + 1] : i % a->H;
-    decode_one(a, b, h, out + (size_t)i * ORC_DV, probs ? probs + (size_t)i * a->max_seq_len : NULL);
+    decode_one(a, q, h, out + (size_t)i * ORC_DV, probs ? probs + (size_t)i * a->max_seq_len : NULL);
   }
   return 0;
 }

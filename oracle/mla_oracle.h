@@ -4,12 +4,13 @@
  * benchmark's CPU-baseline leg; never by the GPU library.
  *
  * All tensors are host arrays, row-major, bf16 passed as raw uint16 bits.
- * Shapes (C = 512 latent, R = 64 rotary, Dn = Dv = 128):
- *   q_nope [B][H][Dn], q_pe [B][H][R], wkv_b [H][Dn+Dv][C]
+ * Shapes (C = 512 latent, R = 64 rotary, Dn = Dv = 128; s query tokens per
+ * sequence):
+ *   q_nope [B][s][H][Dn], q_pe [B][s][H][R], wkv_b [H][Dn+Dv][C]
  *   kv_cache  bf16 [B][max_seq_len][C]  or  E4M3FN codes uint8 [B][max_seq_len][C]
  *   kv_scale  fp32 [B][max_seq_len][C/128] (FP8 cache only)
  *   pe_cache  bf16 [B][max_seq_len][R]
- *   cache_lens int32 [B], topk_idx int32 [B][topk] (topk > 0 only)
+ *   cache_lens int32 [B], topk_idx int32 [B][s][topk] (topk > 0 only)
  */
 #ifndef MLA_ORACLE_H
 #define MLA_ORACLE_H
@@ -22,6 +23,7 @@ extern "C" {
 
 typedef struct oracle_decode_args {
   int B, H, max_seq_len;
+  int s;     /* query tokens per sequence (>= 1): the last s cached positions */
   int fp8;   /* 0: bf16 latent cache; 1: E4M3FN codes + per-128 fp32 scales */
   int topk;  /* 0: dense over [0, end_b); >0: entries per row of topk_idx */
   double softmax_scale;
@@ -49,9 +51,10 @@ int oracle_cache_write(int B, int s, int max_seq_len, int fp8, const uint16_t* k
                        const uint16_t* pe_new, const int32_t* start_pos, void* kv_cache,
                        float* kv_scale, uint16_t* pe_cache);
 
-/* Decode for n_pairs (b, h) pairs (pairs = int32 [n_pairs][2]), or for every
- * (b, h) in b-major order when pairs is NULL.  out: double [n][Dv];
- * probs (optional): double [n][max_seq_len].  Returns 0 on success. */
+/* Decode for n_pairs (q, h) pairs, q = b * s + i the query token i of
+ * sequence b (pairs = int32 [n_pairs][2]), or for every (q, h) in q-major
+ * order when pairs is NULL.  out: double [n][Dv]; probs (optional): double
+ * [n][max_seq_len].  Returns 0 on success. */
 int oracle_decode(const oracle_decode_args* a, int n_pairs, const int32_t* pairs, double* out,
                   double* probs);
 

@@ -19,7 +19,7 @@ C_LATENT, R_ROPE, D_NOPE, D_V, BLOCK = 512, 64, 128, 128, 128
 class _DecodeArgs(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int), ("H", ctypes.c_int), ("max_seq_len", ctypes.c_int),
-        ("fp8", ctypes.c_int), ("topk", ctypes.c_int), ("softmax_scale", ctypes.c_double),
+        ("s", ctypes.c_int), ("fp8", ctypes.c_int), ("topk", ctypes.c_int), ("softmax_scale", ctypes.c_double),
         ("q_nope", ctypes.c_void_p), ("q_pe", ctypes.c_void_p), ("wkv_b", ctypes.c_void_p),
         ("kv_cache", ctypes.c_void_p), ("kv_scale", ctypes.c_void_p),
         ("pe_cache", ctypes.c_void_p), ("cache_lens", ctypes.c_void_p),
@@ -142,12 +142,15 @@ def cache_write(kv_new, pe_new, start_pos, max_seq_len, fp8, kv_cache=None, kv_s
 
 def decode(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, softmax_scale, kv_scale=None,
            topk_idx=None, pairs=None, want_probs=False):
-    """Oracle decode; returns out (float64) [B][H][128] or [n_pairs][128] (+ probs).
+    """Oracle decode; returns out (float64) [B][H][128] for one query token,
+    [B][s][H][128] for s > 1, or [n_pairs][128] (+ probs).
 
-    q_nope [B][1][H][128], q_pe [B][1][H][64], wkv_b [H][256][512] (bf16);
+    q_nope [B][s][H][128], q_pe [B][s][H][64], wkv_b [H][256][512] (bf16);
     kv_cache bf16 [B][T][512] or uint8 E4M3FN codes (then kv_scale fp32 [B][T][4]);
-    pe_cache bf16 [B][T][64]; cache_lens int32 [B]; topk_idx int32 [B][1][k] or None;
-    pairs: optional int array [n][2] of (b, h) to evaluate.
+    pe_cache bf16 [B][T][64]; cache_lens int32 [B]; topk_idx int32 [B][s][k] or None;
+    pairs: optional int array [n][2] of (q, h) to evaluate, q = b * s + i.
+    The s query tokens are the last s cached positions; token i sees rows
+    t < end_b - (s - 1 - i).
     """
     qn = _np(q_nope, np.uint16)
     qp = _np(q_pe, np.uint16)
@@ -159,7 +162,8 @@ def decode(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, softmax_scale, k
     lens = _np(cache_lens, np.int32)
     B, T = kv.shape[0], kv.shape[1]
     H = w.shape[0]
-    assert qn.size == B * H * D_NOPE and qp.size == B * H * R_ROPE
+    s = qn.size // (B * H * D_NOPE) if B > 0 else 1
+    assert qn.size == B * s * H * D_NOPE and qp.size == B * s * H * R_ROPE
     assert w.shape == (H, D_NOPE + D_V, C_LATENT)
     assert kv.shape == (B, T, C_LATENT) and pe.shape == (B, T, R_ROPE) and lens.shape == (B,)
     k = 0
@@ -167,21 +171,21 @@ def decode(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, softmax_scale, k
     if topk_idx is not None:
         ti = _np(topk_idx, np.int32)
         k = ti.shape[-1]
-        assert ti.size == B * k
-    args = _DecodeArgs(B, H, T, int(fp8), k, float(softmax_scale), _ptr(qn), _ptr(qp), _ptr(w),
+        assert ti.size == B * s * k
+    args = _DecodeArgs(B, H, T, s, int(fp8), k, float(softmax_scale), _ptr(qn), _ptr(qp), _ptr(w),
                        _ptr(kv), _ptr(sc), _ptr(pe), _ptr(lens), _ptr(ti))
     if pairs is not None:
         pr = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
         n = pr.shape[0]
     else:
-        pr, n = None, B * H
+        pr, n = None, B * s * H
     out = np.zeros((n, D_V), np.float64)
     probs = np.zeros((n, T), np.float64) if want_probs else None
     rc = lib().oracle_decode(ctypes.byref(args), n, _ptr(pr), _ptr(out), _ptr(probs))
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
     if pairs is None:
-        out = out.reshape(B, H, D_V)
+        out = out.reshape((B, H, D_V) if s == 1 else (B, s, H, D_V))
         if want_probs:
-            probs = probs.reshape(B, H, T)
+            probs = probs.reshape((B, H, T) if s == 1 else (B, s, H, T))
     return (out, probs) if want_probs else out

@@ -399,3 +399,68 @@ def test_fp8_zero_block_gives_zero_scale_and_codes():
     codes, scales, _ = oracle.cache_write(kv, pe, torch.zeros(1, dtype=torch.int32), 1, True)
     assert scales[0, 0, 0] == 0 and scales[0, 0, 2] == 0 and scales[0, 0, 1] > 0
     assert (codes[0, 0, :128] == 0).all() and (codes[0, 0, 256:] == 0).all()
+
+
+# ---------------------------------------------------------------- s > 1 query tokens
+
+def multitoken_inputs(B, s, H, T, seed):
+    g = torch.Generator().manual_seed(seed)
+    bf = lambda *shape, std=1.0: (torch.randn(*shape, generator=g) * std).to(torch.bfloat16)
+    return {"q_nope": bf(B, s, H, 128), "q_pe": bf(B, s, H, 64), "wkv_b": bf(H, 256, 512, std=512 ** -0.5),
+            "kv": bf(B, T, 512), "pe": bf(B, T, 64)}
+
+
+def naive_multitoken(x, sel_of):
+    """Expanded-MHA attention of every query token (b, i) over the rows
+    sel_of(b, i) selects (boolean [T])."""
+    B, s = x["q_nope"].shape[:2]
+    out = np.zeros((B, s, x["q_nope"].shape[2], 128))
+    for b in range(B):
+        for i in range(s):
+            one = {k: x[k][b:b + 1, i:i + 1] for k in ("q_nope", "q_pe")}
+            out[b, i] = naive_mha(f64(one["q_nope"]), f64(one["q_pe"]), f64(x["wkv_b"]),
+                                  f64(x["kv"][b:b + 1]), f64(x["pe"][b:b + 1]), sel_of(b, i)[None, :],
+                                  SCALE)[0]
+    return out
+
+
+def test_multitoken_causal_equals_naive():
+    # token i of s is the (s - i)-th last cached position and sees the rows up
+    # to its own: lengths include one shorter than s (its first tokens see nothing)
+    B, s, H, T = 3, 3, 4, 20
+    x = multitoken_inputs(B, s, H, T, seed=21)
+    lens = torch.tensor([20, 7, 2], dtype=torch.int32)
+    got = oracle.decode(x["q_nope"], x["q_pe"], x["wkv_b"], x["kv"], x["pe"], lens, SCALE)
+    t = np.arange(T)
+    ref = naive_multitoken(x, lambda b, i: t <= int(lens[b]) - s + i)
+    assert got.shape == (B, s, H, 128)
+    assert rel(got, ref) < 1e-12
+    assert (got[2, 0] == 0).all()  # length 2, first of three tokens: no row
+
+
+def test_multitoken_topk_uses_each_tokens_indices():
+    B, s, H, T, k = 2, 2, 4, 40, 9
+    x = multitoken_inputs(B, s, H, T, seed=22)
+    lens = torch.tensor([40, 31], dtype=torch.int32)
+    g = torch.Generator().manual_seed(23)
+    idx = torch.stack([torch.stack([torch.randperm(T, generator=g)[:k] for _ in range(s)]) for _ in range(B)])
+    idx = idx.to(torch.int32)
+    got = oracle.decode(x["q_nope"], x["q_pe"], x["wkv_b"], x["kv"], x["pe"], lens, SCALE, topk_idx=idx)
+    t = np.arange(T)
+
+    def sel(b, i):
+        m = np.zeros(T, bool)
+        m[idx[b, i].numpy()] = True
+        return m & (t <= int(lens[b]) - s + i)
+
+    assert rel(got, naive_multitoken(x, sel)) < 1e-12
+
+
+def test_multitoken_last_token_sees_the_whole_cache():
+    B, s, H, T = 2, 4, 4, 16
+    x = multitoken_inputs(B, s, H, T, seed=24)
+    lens = torch.tensor([16, 11], dtype=torch.int32)
+    got = oracle.decode(x["q_nope"], x["q_pe"], x["wkv_b"], x["kv"], x["pe"], lens, SCALE)
+    ref = naive_mha(f64(x["q_nope"][:, s - 1:]), f64(x["q_pe"][:, s - 1:]), f64(x["wkv_b"]), f64(x["kv"]),
+                    f64(x["pe"]), dense_sel(lens.numpy(), T), SCALE)
+    assert rel(got[:, s - 1], ref) < 1e-12
