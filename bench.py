@@ -111,37 +111,46 @@ def kernel_symbol(name, w):
             "uproj": "mla::uproj_kernel"}[name]
 
 
-def workload_bytes_flops(w, lens, k):
-    """Algorithmic bytes and FLOPs per kernel launch (one step)."""
+def workload_bytes_flops(w, lens, k, s=1):
+    """Algorithmic bytes and FLOPs per kernel launch (one step).  With s query
+    tokens per sequence the cache rows count once per sequence (the method
+    scores all s tokens against them); the FLOPs count the rows each token sees
+    (token i sees len - (s - 1 - i) rows)."""
     B, H = w.batch, w.heads
+    Q = B * s  # query tokens
     rows = [min(k, int(n)) if k else int(n) for n in lens]
+    tok_rows = [min(k, max(0, int(n) - (s - 1 - i))) if k else max(0, int(n) - (s - 1 - i))
+                for n in lens for i in range(s)]
     row_bytes = (512 + 16 + 128) if w.fp8 else (1024 + 128)
-    n_rows = sum(rows)
+    n_rows, n_tok_rows = sum(rows), sum(tok_rows)
     proj_w = 2 * H * 128 * 512
     out = {
-        "absorb": (proj_w + 2 * B * H * 128, 2 * B * H * 128 * 512),
-        "attention": (n_rows * row_bytes + 2 * B * H * 64 + 4 * B + 4 * B * k,
-                      n_rows * H * 2 * (576 + 512)),
+        "absorb": (proj_w + 2 * Q * H * 128, 2 * Q * H * 128 * 512),
+        "attention": (n_rows * row_bytes + 2 * Q * H * 64 + 4 * B + 4 * Q * k,
+                      n_tok_rows * H * 2 * (576 + 512)),
         "combine": (0, 0),
-        "uproj": (proj_w + 2 * B * H * 128, 2 * B * H * 128 * 512),
-        "cache_write": (B * 2 * 576 + B * row_bytes + 4 * B, 0),
+        "uproj": (proj_w + 2 * Q * H * 128, 2 * Q * H * 128 * 512),
+        "cache_write": (Q * 2 * 576 + Q * row_bytes + 4 * B, 0),
     }
     if FUSED:  # the row stores run inside the absorb launch
         out["absorb"] = (out["absorb"][0] + out.pop("cache_write")[0], out["absorb"][1])
-    total_bytes = (2 * B * H * 192 + 2 * proj_w + n_rows * row_bytes + 4 * B + 4 * B * k
-                   + 2 * B * H * 128)
-    total_flops = 4 * B * H * 128 * 512 + n_rows * H * 2 * (576 + 512)
+    total_bytes = (2 * Q * H * 192 + 2 * proj_w + n_rows * row_bytes + 4 * B + 4 * Q * k
+                   + 2 * Q * H * 128)
+    total_flops = 4 * Q * H * 128 * 512 + n_tok_rows * H * 2 * (576 + 512)
     return out, total_bytes, total_flops, n_rows, row_bytes
 
 
 def build_replicas(w, x, R, mla, torch):
     dev = "cuda:0"
     B, T = w.batch, w.max_seq_len
+    s = x["q_nope"].shape[1]
     lens = x["cache_lens"]
-    start = torch.clamp(lens - 1, min=0)
-    rows = start.long()
-    kv_new = x["kv"][torch.arange(B), rows].reshape(B, 1, 512).contiguous()
-    pe_new = x["pe"][torch.arange(B), rows].reshape(B, 1, 64).contiguous()
+    start = torch.clamp(lens - s, min=0)
+    # the new rows are the cache's own last s rows, so every step stores the
+    # same values again
+    rows = (start.long().reshape(B, 1) + torch.arange(s).reshape(1, s)).clamp(max=T - 1)
+    kv_new = x["kv"][torch.arange(B).reshape(B, 1), rows].reshape(B, s, 512).contiguous()
+    pe_new = x["pe"][torch.arange(B).reshape(B, 1), rows].reshape(B, s, 64).contiguous()
     base = {
         "q_nope": x["q_nope"].to(dev), "q_pe": x["q_pe"].to(dev), "wkv_b": x["wkv_b"].to(dev),
         "kv_new": kv_new.to(dev), "pe_new": pe_new.to(dev),
@@ -185,8 +194,9 @@ def cpu_baseline(w, x, seconds, oracle, synth, np, torch):
                                         w.max_seq_len, True)
     else:
         kv, sc, pe = x["kv"], None, x["pe"]
-    total_pairs = w.batch * w.heads
-    pairs_all = [(b, h) for b in range(w.batch) for h in range(w.heads)]
+    Q = w.batch * x["q_nope"].shape[1]  # query tokens
+    total_pairs = Q * w.heads
+    pairs_all = [(q, h) for q in range(Q) for h in range(w.heads)]
     done, t0 = 0, time.perf_counter()
     chunk = max(1, min(total_pairs, 4 * oracle.num_threads()))
     i = 0
@@ -200,10 +210,10 @@ def cpu_baseline(w, x, seconds, oracle, synth, np, torch):
         if el >= seconds and done >= min(total_pairs, chunk):
             break
     steps = done / total_pairs
-    return {"value": w.batch * steps / el, "unit": "tokens/s", "cores": oracle.num_threads(),
+    return {"value": Q * steps / el, "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"{done} (sequence, head) outputs of {w.name} in {el:.1f} s "
-                      f"({steps:.3f} full steps; tokens/s = B x steps / time)"}
+            "sample": f"{done} (query token, head) outputs of {w.name} in {el:.1f} s "
+                      f"({steps:.3f} full steps; tokens/s = query tokens x steps / time)"}
 
 
 def main():
@@ -216,6 +226,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches, not graph replay")
+    ap.add_argument("--seqlen-q", type=int, default=1,
+                    help="query tokens per sequence (the last s cached positions; token i sees "
+                         "the rows up to its own)")
     ap.add_argument("--unfused", action="store_true",
                     help="mla_cache_write then mla_decode instead of mla_decode_step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -247,14 +260,17 @@ def main():
     w = synth.WORKLOADS[args.workload]
     x = synth.make_inputs(w)
     k = w.topk
+    S = args.seqlen_q
+    if S > 1:  # more query tokens per sequence: extra seeded draws of the same distributions
+        x = synth.add_query_tokens(x, S, seed=w.seed + 1000)
     per_kernel, total_bytes, total_flops, n_rows, row_bytes = workload_bytes_flops(
-        w, x["cache_lens"].tolist(), k)
+        w, x["cache_lens"].tolist(), k, S)
     working = total_bytes + 2 * w.batch * w.heads * 128
     R = args.replicas or max(1, min(32, math.ceil(2 * MALL_BYTES / working)))
     reps, shared = build_replicas(w, x, R, mla, torch)
     B, H = w.batch, w.heads
-    out = torch.empty(B, 1, H, 128, dtype=torch.bfloat16, device="cuda:0")
-    p = mla.make_params(B, H, w.max_seq_len, 1 if w.fp8 else 0, topk=k)
+    out = torch.empty(B, S, H, 128, dtype=torch.bfloat16, device="cuda:0")
+    p = mla.make_params(B, H, w.max_seq_len, 1 if w.fp8 else 0, topk=k, seqlen_q=S)
     ws = torch.empty(mla.decode_workspace_size(p), dtype=torch.uint8, device="cuda:0")
 
     for i in range(args.warmup):
@@ -327,7 +343,7 @@ def main():
     roof["kernel"] = dom
     roof["avg_us"] = avg_us[dom]
 
-    tokens_per_s = B * args.steps / elapsed
+    tokens_per_s = B * S * args.steps / elapsed
     step_s = ms_per_step * 1e-3
     latent_bytes = n_rows * row_bytes
     result = {
@@ -344,7 +360,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": w.name, "batch": B, "heads": H, "max_seq_len": w.max_seq_len,
+            "workload": w.name + (f"_s{S}" if S > 1 else ""), "batch": B, "query_tokens": S,
+            "heads": H, "max_seq_len": w.max_seq_len,
             "kv_cache": "fp8_e4m3_block128" if w.fp8 else "bf16",
             "selection": (f"top-{k}" if k else ("ragged U{%d..%d}" % w.ragged if w.ragged else "dense")),
             "rows_per_step": n_rows, "replicas": R,

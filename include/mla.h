@@ -63,7 +63,10 @@ typedef enum mla_kv_dtype {
  * Problem description, passed by pointer (host memory, read during the call).
  *   batch         B >= 0 sequences (B == 0 is a no-op)
  *   seqlen_q      s: new rows per sequence for mla_cache_write (>= 0);
- *                 must be 1 for mla_decode (one query token per sequence)
+ *                 query tokens per sequence for mla_decode / mla_decode_step
+ *                 (>= 1, batch * s <= 65535): the s tokens are the last s
+ *                 cached positions of the sequence, and token i (0-based)
+ *                 sees the rows up to its own, t < end_b - (s - 1 - i)
  *   num_heads     H, 1..128 (the local heads of this GPU)
  *   max_seq_len   T: second dimension of every cache buffer, >= 1
  *   kv_lora_rank, qk_nope_dim, qk_rope_dim, v_head_dim: must be 512, 128, 64, 128
@@ -131,30 +134,32 @@ mla_status mla_decode_workspace_size(const mla_params* p, size_t* bytes);
 /*
  * mla_decode -- one decode step of weight-absorbed MLA for every sequence.
  *
- * Follows the "MQA decode" excerpt of "DeepSeek-V3.2-Exp . KV cache" and
- * sections 3-4 of the MLA article, per sequence b and head h:
- *   1. absorb:  qa[c]   = sum_d q_nope[b,0,h,d] * wkv_b[h,d,c]          (d < 128)
- *   2. score:   S[t]    = (qa . c_KV[b,t] + q_pe[b,0,h] . k_R[b,t]) * softmax_scale
- *   3. softmax over the selected positions t (dense: t < end_b; top-k: the
- *      set of entries of topk_idx[b] inside [0, end_b))
+ * Follows the "MQA decode" excerpt of "DeepSeek-V3.2-Exp . KV cache" (whose
+ * einsums carry the query-token dimension s) and sections 3-4 of the MLA
+ * article, per sequence b, query token i < s and head h:
+ *   1. absorb:  qa[c]   = sum_d q_nope[b,i,h,d] * wkv_b[h,d,c]          (d < 128)
+ *   2. score:   S[t]    = (qa . c_KV[b,t] + q_pe[b,i,h] . k_R[b,t]) * softmax_scale
+ *   3. softmax over the selected positions t (dense: t < e; top-k: the set
+ *      of entries of topk_idx[b,i] inside [0, e))
  *   4. reduce:  o[c]    = sum_t p[t] * c_KV[b,t,c]
- *   5. up-project: out[b,0,h,d] = sum_c o[c] * wkv_b[h,128+d,c]
- * with end_b = min(max(cache_lens[b], 0), T).  c_KV is the bf16 latent, or for
- * the FP8 cache bf16(float(code) * scale).
+ *   5. up-project: out[b,i,h,d] = sum_c o[c] * wkv_b[h,128+d,c]
+ * with end_b = min(max(cache_lens[b], 0), T) and e = end_b - (s - 1 - i)
+ * (e = end_b for one query token).  c_KV is the bf16 latent, or for the FP8
+ * cache bf16(float(code) * scale).
  *
- *   q_nope     bf16 [B][1][H][128]
- *   q_pe       bf16 [B][1][H][64] (already rotated)
+ *   q_nope     bf16 [B][s][H][128]
+ *   q_pe       bf16 [B][s][H][64] (already rotated)
  *   wkv_b      bf16 [H][256][512]: rows 0..127 the key half W_UK, rows
  *              128..255 the value half W_UV of each head
  *   kv_cache, kv_scale, pe_cache: as for mla_cache_write
  *   cache_lens int32 [B] (device): rows 0..cache_lens[b]-1 are valid
- *   topk_idx   int32 [B][1][topk] (device) when topk > 0, else NULL.  Entries
- *              outside [0, end_b) (e.g. -1 padding) are skipped; the valid
- *              entries of a row must be distinct.
- *   out        bf16 [B][1][H][128]
+ *   topk_idx   int32 [B][s][topk] (device) when topk > 0, else NULL: one row
+ *              per query token.  Entries outside [0, e) (e.g. -1 padding)
+ *              are skipped; the valid entries of a row must be distinct.
+ *   out        bf16 [B][s][H][128]
  *   workspace  device scratch of at least mla_decode_workspace_size() bytes,
  *              16-byte aligned; its contents are undefined after the call.
- * A sequence with no selected position gets an output row of zeros.
+ * A query token with no selected position gets an output row of zeros.
  */
 mla_status mla_decode(const mla_params* p, const void* q_nope, const void* q_pe,
                       const void* wkv_b, const void* kv_cache, const float* kv_scale,
@@ -168,15 +173,15 @@ mla_status mla_decode(const mla_params* p, const void* q_nope, const void* q_pe,
  * A decoding token's own compressed row joins the cache before its query
  * attends ("DeepSeek-V3.2-Exp . KV cache", the cache-write and "MQA decode"
  * excerpts; MLA article section 3, the cached latent per token).  The result
- * equals mla_cache_write with s = 1 and start_pos[b] = cache_lens[b] - 1,
+ * equals mla_cache_write with the same s and start_pos[b] = cache_lens[b] - s,
  * followed by mla_decode with the same arguments, but needs no extra launch:
  * the row stores run in spare workgroups of the absorb kernel.
  *
- *   kv_new     bf16 [B][1][512]: new latent row c_KV of each sequence
- *   pe_new     bf16 [B][1][64]:  new rotary row k_R (already rotated)
- *   kv_cache, kv_scale, pe_cache: as for mla_cache_write, written at row
- *              cache_lens[b] - 1 of sequence b (nothing is written where that
- *              row is outside [0, T)), then read as for mla_decode
+ *   kv_new     bf16 [B][s][512]: new latent rows c_KV of each sequence
+ *   pe_new     bf16 [B][s][64]:  new rotary rows k_R (already rotated)
+ *   kv_cache, kv_scale, pe_cache: as for mla_cache_write, written at rows
+ *              cache_lens[b] - s .. cache_lens[b] - 1 of sequence b (rows
+ *              outside [0, T) are not written), then read as for mla_decode
  *   every other argument, the workspace size and the trace events: as for
  *   mla_decode (the row stores are part of kernel 0's time)
  * Checks, errors and a rejected call enqueue nothing, as for mla_decode.  Two

@@ -99,6 +99,7 @@ mla_status mla_decode_workspace_size(const mla_params* p, size_t* bytes) {
     return fail(MLA_ERR_INVALID_ARG, "num_heads = %d outside 1..128", p->num_heads);
   if (p->topk < 0 || p->topk > p->max_seq_len)
     return fail(MLA_ERR_INVALID_ARG, "topk = %d outside 0..max_seq_len", p->topk);
+  if (p->seqlen_q < 1) return fail(MLA_ERR_INVALID_ARG, "seqlen_q = %d < 1", p->seqlen_q);
   const mla::DecodePlan plan = mla::make_decode_plan(*p);
   if (plan.max_groups > 0x7FFFFFFFLL || plan.max_groups * plan.heads_padded > (1LL << 40))
     return fail(MLA_ERR_UNSUPPORTED, "too many attention workgroups for this batch and top-k");
@@ -118,15 +119,15 @@ mla_status check_decode(const mla_params* p, const void* q_nope, const void* q_p
                         void* out, void* workspace, size_t workspace_bytes, mla::DecodePlan* plan) {
   mla_status st = check_params(p);
   if (st != MLA_OK) return st;
-  if (p->seqlen_q != 1)
-    return fail(MLA_ERR_UNSUPPORTED, "seqlen_q = %d; decode implements one query token", p->seqlen_q);
+  if (p->seqlen_q < 1) return fail(MLA_ERR_INVALID_ARG, "seqlen_q = %d < 1", p->seqlen_q);
   if (p->num_heads < 1 || p->num_heads > MLA_MAX_HEADS)
     return fail(MLA_ERR_INVALID_ARG, "num_heads = %d outside 1..128", p->num_heads);
   if (p->topk < 0 || p->topk > p->max_seq_len)
     return fail(MLA_ERR_INVALID_ARG, "topk = %d outside 0..max_seq_len", p->topk);
   if (!(p->softmax_scale > 0.0f) || !isfinite(p->softmax_scale))
     return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
-  if (p->batch > 65535) return fail(MLA_ERR_UNSUPPORTED, "batch > 65535");
+  if ((long long)p->batch * p->seqlen_q > 65535)
+    return fail(MLA_ERR_UNSUPPORTED, "batch * seqlen_q > 65535 query tokens");
   if (p->batch == 0) return MLA_OK;
   const bool fp8 = p->kv_dtype == MLA_KV_FP8_E4M3_B128;
   if (!q_nope || !q_pe || !wkv_b || !kv_cache || !pe_cache || !cache_lens || !out)

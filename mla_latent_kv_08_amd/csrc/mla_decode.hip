@@ -25,6 +25,12 @@ __device__ __forceinline__ int seq_len(const int32_t* lens, int b, int T) {
   const int len = lens[b];
   return len < 0 ? 0 : (len > T ? T : len);
 }
+// Rows seen by query token v = b * s + i (the last s cached positions are the
+// s query tokens; token i sees the rows up to its own).
+__device__ __forceinline__ int query_len(const int32_t* lens, int v, int s, int T) {
+  const int len = s == 1 ? seq_len(lens, v, T) : seq_len(lens, v / s, T) - (s - 1 - v % s);
+  return len < 0 ? 0 : len;
+}
 __device__ __forceinline__ int selected_entries(int len, int topk) {
   return topk > 0 ? (len > 0 ? topk : 0) : len;
 }
@@ -107,7 +113,9 @@ __device__ __forceinline__ int xcd_workgroup(int s, int n) {
 }
 
 // Work plan of one decode call, computed by one workgroup of 256 threads (the
-// split is described with make_decode_plan): picks the tile budget S, then
+// split is described with make_decode_plan) over the B query tokens (B = batch
+// x tokens per sequence, token v = b s + i seeing query_len rows of sequence
+// v / s): picks the tile budget S, then
 // writes wcum[b] = k_0 + ... + k_{b-1} (wcum[B] = workgroups in use) and, for
 // each of the G attention workgroups, the record {sequence, first tile, end
 // tile, clamped length} (sequence -1: workgroup unused) and the plan slot its
@@ -128,8 +136,8 @@ __device__ __forceinline__ long long ceil_div(long long a, long long b) {
 // LDS of the planner (the caller's buffer, kPlanLdsBytes).
 constexpr int kPlanLdsBytes = 12 * 8 + 4 * 4 + (3 * kPlanCache + 1) * 4 + 32 * 4;
 
-__device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min_tiles, int G,
-                            int32_t* wcum, int4* rec, int32_t* slot_of, char* lds) {
+__device__ void plan_groups(const int32_t* lens, int B, int s, int T, int topk, int min_tiles,
+                            int G, int32_t* wcum, int4* rec, int32_t* slot_of, char* lds) {
   long long* red = (long long*)lds;           // [12]
   int* sc = (int*)(lds + 96);                 // [4]
   int* tl = sc + 4;                           // [kPlanCache] tiles of sequence b
@@ -137,12 +145,12 @@ __device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min
   int* sw = sl + kPlanCache;                  // [kPlanCache + 1] first workgroup of sequence b
   const int tid = threadIdx.x;
   auto tiles_of = [&](int bb) -> int {
-    return (selected_entries(seq_len(lens, bb, T), topk) + kTileRows - 1) / kTileRows;
+    return (selected_entries(query_len(lens, bb, s, T), topk) + kTileRows - 1) / kTileRows;
   };
   auto tiles = [&](int bb) -> int { return bb < kPlanCache ? tl[bb] : tiles_of(bb); };
   long long tot = 0, mx = 0, nonempty = 0;
   for (int bb = tid; bb < B; bb += 256) {
-    const int len = seq_len(lens, bb, T);
+    const int len = query_len(lens, bb, s, T);
     const int t = (selected_entries(len, topk) + kTileRows - 1) / kTileRows;
     if (bb < kPlanCache) {
       tl[bb] = t;
@@ -223,7 +231,7 @@ __device__ void plan_groups(const int32_t* lens, int B, int T, int topk, int min
       wcum[bb + 1] = run + incl;
       if (bb <= kPlanCache) sw[bb] = run + incl - k;
       if (bb >= kPlanCache) {  // long batches: these records come from the sequence's own thread
-        const int t = tiles_of(bb), len = seq_len(lens, bb, T);
+        const int t = tiles_of(bb), len = query_len(lens, bb, s, T);
         for (int p = 0; p < k; ++p)
           put(run + incl - k + p,
               make_int4(bb, (int)floor_div((long long)p * t, k), (int)floor_div((long long)(p + 1) * t, k), len));
@@ -265,27 +273,29 @@ struct RowWrite {
   uint16_t* pe;            // [B][T][64]
 };
 
-// Writer workgroup w of nw: bf16 rows as 72 16-byte chunks per thread item,
-// FP8 rows as four 128-element blocks per wavefront item.
+// Writer workgroup w of nw: the new rows of the Bq = batch x s query tokens,
+// token v = b s + i at cache row cache_lens[b] - s + i; bf16 rows as 72
+// 16-byte chunks per thread item, FP8 rows as four 128-element blocks per
+// wavefront item.
 template <int WRITE>
-__device__ __forceinline__ void write_new_rows(const RowWrite& rw, const int32_t* lens, int B, int T,
-                                               int w, int nw) {
+__device__ __forceinline__ void write_new_rows(const RowWrite& rw, const int32_t* lens, int Bq, int s,
+                                               int T, int w, int nw) {
   const int tid = threadIdx.x;
   if (WRITE == kWriteBf16) {
-    for (long long g = (long long)w * 256 + tid; g < (long long)B * 72; g += (long long)nw * 256) {
-      const int b = (int)(g / 72), ch = (int)(g % 72);
-      const long long r = (long long)lens[b] - 1;
+    for (long long g = (long long)w * 256 + tid; g < (long long)Bq * 72; g += (long long)nw * 256) {
+      const int v = (int)(g / 72), ch = (int)(g % 72), b = v / s;
+      const long long r = (long long)lens[b] - s + (v - b * s);
       if (r < 0 || r >= T) continue;
-      store_row_chunk_bf16(rw.kv_new, rw.pe_new, (uint16_t*)rw.kv, rw.pe, (size_t)b,
+      store_row_chunk_bf16(rw.kv_new, rw.pe_new, (uint16_t*)rw.kv, rw.pe, (size_t)v,
                            (size_t)b * T + (size_t)r, ch);
     }
   } else if (WRITE == kWriteFp8) {
     const int lane = tid & 63;
-    for (long long g = (long long)w * 4 + (tid >> 6); g < (long long)B * 4; g += (long long)nw * 4) {
-      const int b = (int)(g >> 2), blk = (int)(g & 3);
-      const long long r = (long long)lens[b] - 1;
+    for (long long g = (long long)w * 4 + (tid >> 6); g < (long long)Bq * 4; g += (long long)nw * 4) {
+      const int v = (int)(g >> 2), blk = (int)(g & 3), b = v / s;
+      const long long r = (long long)lens[b] - s + (v - b * s);
       if (r < 0 || r >= T) continue;  // uniform per wave
-      store_row_block_fp8(rw.kv_new, rw.pe_new, (uint8_t*)rw.kv, rw.kv_scale, rw.pe, (size_t)b,
+      store_row_block_fp8(rw.kv_new, rw.pe_new, (uint8_t*)rw.kv, rw.kv_scale, rw.pe, (size_t)v,
                           (size_t)b * T + (size_t)r, blk, lane);
     }
   }
@@ -293,11 +303,11 @@ __device__ __forceinline__ void write_new_rows(const RowWrite& rw, const int32_t
 
 // ---------------------------------------------------------------------------
 // absorb: grid (heads_padded + 1 + writer columns, 4 column blocks of 128,
-// sequence ranges), 256 threads.  Workgroup (heads_padded, 0, 0) computes the
-// attention work plan instead; in the fused step the workgroups of the writer
-// columns (z = 0) store the new cache row of every sequence at position
-// cache_lens[b] - 1 (before the attention kernel, which is launched after
-// this one, reads the caches).
+// query-token ranges), 256 threads.  B counts query tokens (batch x s).
+// Workgroup (heads_padded, 0, 0) computes the attention work plan instead; in
+// the fused step the workgroups of the writer columns (z = 0) store the new
+// cache rows of every sequence at positions cache_lens[b] - s .. - 1 (before
+// the attention kernel, which is launched after this one, reads the caches).
 //
 // Head h, columns 128y..128y+127: the W_UK slice (128 d x 128 c) is staged in
 // LDS and held as MFMA B fragments, wave w taking 32 columns; each block of 32
@@ -312,7 +322,7 @@ template <int WRITE>
 __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict__ q_nope,
                                                      const uint16_t* __restrict__ q_pe,
                                                      const uint16_t* __restrict__ wkv_b,
-                                                     uint16_t* __restrict__ qt, int B, int H,
+                                                     uint16_t* __restrict__ qt, int B, int s, int H,
                                                      int Hp, int bz, const int32_t* __restrict__ lens,
                                                      int T, int topk, int min_group_tiles,
                                                      int G, int32_t* wcum, int4* rec,
@@ -326,9 +336,9 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
   if (h >= Hp) {
     if (blockIdx.z != 0) return;
     if (h == Hp) {
-      if (cblk == 0) plan_groups(lens, B, T, topk, min_group_tiles, G, wcum, rec, slot_of, smem);
+      if (cblk == 0) plan_groups(lens, B, s, T, topk, min_group_tiles, G, wcum, rec, slot_of, smem);
     } else if (WRITE != kNoWrite) {
-      write_new_rows<WRITE>(rw, lens, B, T, (h - Hp - 1) * 4 + cblk, (gridDim.x - Hp - 1) * 4);
+      write_new_rows<WRITE>(rw, lens, B, s, T, (h - Hp - 1) * 4 + cblk, (gridDim.x - Hp - 1) * 4);
     }
     return;
   }
@@ -458,7 +468,7 @@ struct AttnArgs {
   const int32_t* slot_of; // [grid] plan slot (partial index) of each workgroup
   uint16_t* part_o;       // [grid][H][512]
   float* part_ml;         // [grid][H][2]
-  int B, H, Hp, T, topk, head_blocks;
+  int B, s, H, Hp, T, topk, head_blocks;  // B: query tokens (batch x s)
   float scale_log2;
 };
 
@@ -537,7 +547,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   const int n_b = TOPK ? (len > 0 ? a.topk : 0) : len;
   const int p0 = t_lo * kTT, p1 = min(t_hi * kTT, n_b);
   const int ntiles = t_hi - t_lo;
-  const size_t seq_row0 = (size_t)b * a.T;
+  const size_t seq_row0 = (size_t)(a.s == 1 ? b : b / a.s) * a.T;  // b: query token
   const size_t slot_id = part_slot;
 
   // One LDS array per ring slot (not one 2-D array): the slot a tile lives in
@@ -1380,7 +1390,7 @@ __global__ __launch_bounds__(64) void uproj_kernel(const uint16_t* __restrict__ 
 hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWriteArgs* write,
                          hipStream_t stream) {
   const DecodePlan plan = make_decode_plan(p);
-  const int B = p.batch, H = p.num_heads;
+  const int s = p.seqlen_q, B = p.batch * s, H = p.num_heads;  // B: query tokens
   char* ws = (char*)d.workspace;
   uint16_t* qt = (uint16_t*)(ws + plan.off_qt);
   uint16_t* part_o = (uint16_t*)(ws + plan.off_part_o);
@@ -1410,7 +1420,7 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
   const int bz = 32 * ((chunks + zs - 1) / zs);
   err = launch_kernel(absorb, dim3(plan.heads_padded + 1 + write_cols, 4, (B + bz - 1) / bz),
                       dim3(256), stream, evk(0), (const uint16_t*)d.q_nope, (const uint16_t*)d.q_pe,
-                      (const uint16_t*)d.wkv_b, qt, B, H, plan.heads_padded, bz, d.cache_lens,
+                      (const uint16_t*)d.wkv_b, qt, B, s, H, plan.heads_padded, bz, d.cache_lens,
                       p.max_seq_len, p.topk, plan.min_group_tiles, (int)plan.max_groups, wcum, rec,
                       slot_of, rw);
   if (err != hipSuccess) return err;
@@ -1426,6 +1436,7 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
   aa.part_o = part_o;
   aa.part_ml = part_ml;
   aa.B = B;
+  aa.s = s;
   aa.H = H;
   aa.Hp = plan.heads_padded;
   aa.T = p.max_seq_len;

@@ -39,7 +39,9 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 inline DecodePlan make_decode_plan(const mla_params& p) {
   DecodePlan d{};
-  const int B = p.batch, H = p.num_heads;
+  // B: query tokens, batch x seqlen_q (each token is planned as a sequence of
+  // its own over the rows it sees)
+  const int B = p.batch * (p.seqlen_q > 0 ? p.seqlen_q : 1), H = p.num_heads;
   d.heads_padded = (H + 31) / 32 * 32;
   d.head_blocks = d.heads_padded / 32;
   const long long n_max = p.topk > 0 ? p.topk : p.max_seq_len;
@@ -52,7 +54,7 @@ inline DecodePlan make_decode_plan(const mla_params& p) {
   }
   d.max_groups = G;
   size_t off = 0;
-  d.off_qt = off;  // bf16 [B][heads_padded][576], in the attention kernel's fragment order
+  d.off_qt = off;  // bf16 [B tokens][heads_padded][576], in the attention kernel's fragment order
   off = align256(off + (size_t)B * d.heads_padded * 576 * 2);
   d.off_part_o = off;  // bf16 [max_groups][heads_padded][512], in fragment order
   off = align256(off + (size_t)G * d.heads_padded * 512 * 2);

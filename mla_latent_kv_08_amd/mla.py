@@ -118,19 +118,21 @@ def cache_write(kv_new, pe_new, start_pos, kv_cache, pe_cache, kv_scale=None, st
 def decode(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, kv_scale=None, topk_idx=None,
            out=None, workspace=None, softmax_scale=DEFAULT_SOFTMAX_SCALE, stream=None,
            trace_events=None):
-    """mla_decode: returns out [B,1,H,128] bf16 (allocated when not given).
+    """mla_decode: returns out [B,s,H,128] bf16 (allocated when not given).
 
-    q_nope [B,1,H,128], q_pe [B,1,H,64], wkv_b [H,256,512] bf16; caches as for
-    cache_write; cache_lens int32 [B]; topk_idx int32 [B,1,k] or None.
+    q_nope [B,s,H,128], q_pe [B,s,H,64], wkv_b [H,256,512] bf16; caches as for
+    cache_write; cache_lens int32 [B]; topk_idx int32 [B,s,k] or None.  The s
+    query tokens are the last s cached positions; token i sees rows
+    t < cache_lens - (s - 1 - i).
     """
     _dev(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, kv_scale, topk_idx, out, workspace)
-    B, H = q_nope.shape[0], q_nope.shape[2]
+    B, s, H = q_nope.shape[0], q_nope.shape[1], q_nope.shape[2]
     fp8 = kv_scale is not None
     k = 0 if topk_idx is None else topk_idx.shape[-1]
     p = make_params(B, H, kv_cache.shape[1], KV_FP8_E4M3_B128 if fp8 else KV_BF16, topk=k,
-                    softmax_scale=softmax_scale, trace_events=trace_events)
+                    seqlen_q=s, softmax_scale=softmax_scale, trace_events=trace_events)
     if out is None:
-        out = torch.empty(B, 1, H, D_V, dtype=torch.bfloat16, device=q_nope.device)
+        out = torch.empty(B, s, H, D_V, dtype=torch.bfloat16, device=q_nope.device)
     if workspace is None:
         workspace = torch.empty(max(decode_workspace_size(p), 16), dtype=torch.uint8,
                                 device=q_nope.device)
@@ -143,22 +145,22 @@ def decode(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, kv_scale=None, t
 def decode_step(kv_new, pe_new, q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens,
                 kv_scale=None, topk_idx=None, out=None, workspace=None,
                 softmax_scale=DEFAULT_SOFTMAX_SCALE, stream=None, trace_events=None):
-    """mla_decode_step: store row cache_lens[b] - 1, then decode; returns out.
+    """mla_decode_step: store rows cache_lens[b] - s .. - 1, then decode; returns out.
 
-    kv_new [B,1,512] and pe_new [B,1,64] bf16; every other argument as for
+    kv_new [B,s,512] and pe_new [B,s,64] bf16; every other argument as for
     decode (the caches are written).
     """
     _dev(kv_new, pe_new, q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, kv_scale, topk_idx,
          out, workspace)
-    B, H = q_nope.shape[0], q_nope.shape[2]
-    if kv_new.shape[0] != B or pe_new.shape[0] != B:
-        raise ValueError("kv_new and pe_new need one row per sequence")
+    B, s, H = q_nope.shape[0], q_nope.shape[1], q_nope.shape[2]
+    if tuple(kv_new.shape[:2]) != (B, s) or tuple(pe_new.shape[:2]) != (B, s):
+        raise ValueError("kv_new and pe_new need one row per query token")
     fp8 = kv_scale is not None
     k = 0 if topk_idx is None else topk_idx.shape[-1]
     p = make_params(B, H, kv_cache.shape[1], KV_FP8_E4M3_B128 if fp8 else KV_BF16, topk=k,
-                    softmax_scale=softmax_scale, trace_events=trace_events)
+                    seqlen_q=s, softmax_scale=softmax_scale, trace_events=trace_events)
     if out is None:
-        out = torch.empty(B, 1, H, D_V, dtype=torch.bfloat16, device=q_nope.device)
+        out = torch.empty(B, s, H, D_V, dtype=torch.bfloat16, device=q_nope.device)
     if workspace is None:
         workspace = torch.empty(max(decode_workspace_size(p), 16), dtype=torch.uint8,
                                 device=q_nope.device)

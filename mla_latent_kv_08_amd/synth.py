@@ -110,3 +110,17 @@ def make_inputs(w: Workload, seed: Optional[int] = None, poison_tail: bool = Fal
         pe[tail] = fill
     return dict(q_nope=q_nope, q_pe=q_pe, wkv_b=wkv_b, kv=kv, pe=pe, cache_lens=lens,
                 topk_idx=topk_idx)
+
+
+def add_query_tokens(x: dict, s: int, seed: int) -> dict:
+    """Inputs with s query tokens per sequence: the workload's token first,
+    then s - 1 more seeded draws of the same distributions (q ~ N(0, 1)); a
+    top-k index row is repeated for every token."""
+    g = torch.Generator().manual_seed(seed)
+    B, _, H, _ = x["q_nope"].shape
+    y = dict(x)
+    y["q_nope"] = torch.cat([x["q_nope"], torch.randn(B, s - 1, H, 128, generator=g).to(torch.bfloat16)], 1)
+    y["q_pe"] = torch.cat([x["q_pe"], torch.randn(B, s - 1, H, 64, generator=g).to(torch.bfloat16)], 1)
+    if x["topk_idx"] is not None:
+        y["topk_idx"] = x["topk_idx"].expand(B, s, x["topk_idx"].shape[-1]).contiguous()
+    return y

@@ -63,7 +63,8 @@ def _decode(m, p, **kw):
 def test_decode_rejects_bad_arguments(m):
     P = m.make_params
     assert m.lib.mla_decode(None, *([None] * 10), 0, None) == 1
-    assert _decode(m, P(1, 128, 4096, seqlen_q=2)) == 2                 # s > 1
+    assert _decode(m, P(1, 128, 4096, seqlen_q=0)) == 1                 # no query token
+    assert _decode(m, P(40000, 16, 100, seqlen_q=2)) == 2               # > 65535 query tokens
     assert _decode(m, P(1, 0, 4096)) == 1                               # no heads
     assert _decode(m, P(1, 129, 4096)) == 1                             # too many heads
     assert _decode(m, P(1, 16, 0)) == 1                                 # empty cache buffer
@@ -120,8 +121,13 @@ def test_workspace_size_is_host_only_and_monotone(m):
     assert m.decode_workspace_size(m.make_params(512, 128, 4096)) > sizes[1]
     small_k = m.decode_workspace_size(m.make_params(8, 128, 65536, topk=2048))
     assert m.decode_workspace_size(m.make_params(8, 128, 65536, topk=65536)) > small_k
+    # s query tokens per sequence plan like batch x s sequences
+    assert m.decode_workspace_size(m.make_params(8, 128, 4096, seqlen_q=4)) == \
+        m.decode_workspace_size(m.make_params(32, 128, 4096))
     with pytest.raises(m.MLAError):
         m.decode_workspace_size(m.make_params(8, 200, 4096))
+    with pytest.raises(m.MLAError):
+        m.decode_workspace_size(m.make_params(8, 128, 4096, seqlen_q=0))
 
 
 def test_decode_step_rejects_bad_arguments(m):
@@ -138,6 +144,6 @@ def test_decode_step_rejects_bad_arguments(m):
     assert step(P(1, 16, 100), kv_new=None) == 1
     assert step(P(1, 16, 100), pe_new=ctypes.c_void_p(0x100004)) == 1      # misaligned
     assert step(P(1, 16, 100, kv_dtype=1)) == 1                             # fp8 without scales
-    assert step(P(1, 16, 100, seqlen_q=2)) == 2
+    assert step(P(1, 16, 100, seqlen_q=0)) == 1
     assert step(P(1, 16, 100), ws_bytes=16) == 3
     assert step(P(0, 16, 100), kv_new=None) == 0                            # empty batch: no-op

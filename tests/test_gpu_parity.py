@@ -294,3 +294,97 @@ def test_decode_step_writes_then_attends(m, fp8, topk, B):
                   kv_scale=sc2)
     out2 = m.decode(*args, kv2, pe2, to_dev(lens), kv_scale=sc2, topk_idx=to_dev(x["topk_idx"]))
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+# ---------------------------------------------------------------- s > 1 query tokens
+
+def multitoken_case(B, s, H, T, fp8, topk, seed):
+    g = torch.Generator().manual_seed(seed)
+    bf = lambda *shape, std=1.0: (torch.randn(*shape, generator=g) * std).to(torch.bfloat16)
+    x = {"q_nope": bf(B, s, H, 128), "q_pe": bf(B, s, H, 64), "wkv_b": bf(H, 256, 512, std=512 ** -0.5),
+         "kv": bf(B, T, 512), "pe": bf(B, T, 64)}
+    lens = torch.randint(s, T + 1, (B,), generator=g, dtype=torch.int32)
+    lens[0] = T
+    if B > 2:
+        lens[2] = s - 1  # its first token sees no row
+    x["cache_lens"] = lens
+    x["topk_idx"] = None
+    if topk:
+        idx = torch.stack([torch.stack([torch.randperm(T, generator=g)[:topk] for _ in range(s)])
+                           for _ in range(B)]).to(torch.int32)
+        idx[0, 0, :5] = -1
+        x["topk_idx"] = idx
+    return x
+
+
+def host_caches(x, T, fp8):
+    """Caches as host tensors: bf16 as drawn, or the oracle's FP8 codes and scales."""
+    if not fp8:
+        return x["kv"], None, x["pe"]
+    B = x["kv"].shape[0]
+    codes, scales, pe = oracle.cache_write(x["kv"], x["pe"], torch.zeros(B, dtype=torch.int32), T, True)
+    return torch.from_numpy(codes), torch.from_numpy(scales), torch.from_numpy(pe.view(np.int16)).view(torch.bfloat16)
+
+
+@pytest.mark.parametrize("B,s,H,T,fp8,topk", [(3, 3, 32, 150, False, 0), (2, 2, 128, 300, False, 0),
+                                              (3, 4, 16, 97, True, 0), (2, 2, 128, 400, False, 64)])
+def test_multitoken_decode(m, B, s, H, T, fp8, topk):
+    x = multitoken_case(B, s, H, T, fp8, topk, seed=31 + s + T)
+    kv, sc, pe = host_caches(x, T, fp8)
+    print(f"[multitoken] B={B} s={s} H={H} T={T} fp8={fp8} topk={topk}", flush=True)
+    out = m.decode(to_dev(x["q_nope"]), to_dev(x["q_pe"]), to_dev(x["wkv_b"]), to_dev(kv), to_dev(pe),
+                   to_dev(x["cache_lens"]), kv_scale=to_dev(sc), topk_idx=to_dev(x["topk_idx"]))
+    torch.cuda.synchronize()
+    ref = oracle.decode(x["q_nope"], x["q_pe"], x["wkv_b"], kv, pe, x["cache_lens"], synth.SOFTMAX_SCALE,
+                        kv_scale=None if sc is None else sc.numpy(), topk_idx=x["topk_idx"])
+    assert tuple(out.shape) == (B, s, H, 128)
+    check(out, ref, fp8, f"multitoken B{B} s{s} H{H}")
+    if B > 2:
+        assert (out[2, 0].float() == 0).all()
+
+
+def test_multitoken_full_size_sampled(m):
+    B, s, H, T = 4, 2, 128, 4096
+    x = multitoken_case(B, s, H, T, False, 0, seed=41)
+    print(f"[multitoken] B={B} s={s} H={H} T={T} sampled", flush=True)
+    out = m.decode(to_dev(x["q_nope"]), to_dev(x["q_pe"]), to_dev(x["wkv_b"]), to_dev(x["kv"]),
+                   to_dev(x["pe"]), to_dev(x["cache_lens"]))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(42)
+    pairs = [(int(q), int(h)) for q, h in zip(rng.integers(0, B * s, 48), rng.integers(0, H, 48))]
+    ref = oracle.decode(x["q_nope"], x["q_pe"], x["wkv_b"], x["kv"], x["pe"], x["cache_lens"],
+                        synth.SOFTMAX_SCALE, pairs=pairs)
+    got = out.reshape(B * s, H, 128)[[p[0] for p in pairs], [p[1] for p in pairs]]
+    check(got, ref, False, "multitoken sampled")
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_multitoken_decode_step(m, fp8):
+    B, s, H, T = 3, 2, 64, 120
+    x = multitoken_case(B, s, H, T, fp8, 0, seed=51)
+    kv_h, sc_h, pe_h = host_caches(x, T, fp8)
+    g = torch.Generator().manual_seed(52)
+    kv_new = torch.randn(B, s, 512, generator=g).to(torch.bfloat16)
+    pe_new = torch.randn(B, s, 64, generator=g).to(torch.bfloat16)
+    lens = x["cache_lens"]
+    print(f"[multitoken step] B={B} s={s} fp8={fp8}", flush=True)
+    kv, sc, pe = to_dev(kv_h), to_dev(sc_h), to_dev(pe_h)
+    args = [to_dev(x["q_nope"]), to_dev(x["q_pe"]), to_dev(x["wkv_b"])]
+    out = m.decode_step(to_dev(kv_new), to_dev(pe_new), *args, kv, pe, to_dev(lens), kv_scale=sc)
+    torch.cuda.synchronize()
+    u16 = lambda t: t.view(torch.int16).numpy().view(np.uint16).copy()
+    okv, osc, ope = oracle.cache_write(kv_new, pe_new, (lens - s).to(torch.int32), T, fp8,
+                                       kv_cache=kv_h.numpy().copy() if fp8 else u16(kv_h),
+                                       kv_scale=None if sc_h is None else sc_h.numpy().copy(),
+                                       pe_cache=u16(pe_h))
+    got_kv = kv.cpu().numpy() if fp8 else kv.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got_kv, okv), "latent cache differs"
+    assert np.array_equal(pe.cpu().view(torch.int16).numpy().view(np.uint16), ope), "rotary cache differs"
+    if fp8:
+        assert np.array_equal(sc.cpu().numpy().view(np.uint32), osc.view(np.uint32)), "scales differ"
+    ref = oracle.decode(x["q_nope"], x["q_pe"], x["wkv_b"], okv, ope, lens, synth.SOFTMAX_SCALE, kv_scale=osc)
+    check(out, ref, fp8, f"multitoken step fp8={fp8}")
+    kv2, sc2, pe2 = to_dev(kv_h), to_dev(sc_h), to_dev(pe_h)
+    m.cache_write(to_dev(kv_new), to_dev(pe_new), to_dev((lens - s).to(torch.int32)), kv2, pe2, kv_scale=sc2)
+    out2 = m.decode(*args, kv2, pe2, to_dev(lens), kv_scale=sc2)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
