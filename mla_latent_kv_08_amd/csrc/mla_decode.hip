@@ -359,13 +359,24 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
   }
   uint16_t(*sW)[kWRow] = (uint16_t(*)[kWRow])smem;  // W_UK[h][d][128y + c]
   uint16_t(*sD)[kWRow] = (uint16_t(*)[kWRow])smem;  // output tile [b][c], after the fragments
+  const int lane = tid & 63, wave = tid >> 6;
+  const int cc = 32 * wave + (lane & 31), kg = lane >> 5;
+  // A operand of a block of 32 query tokens: lane holds q_nope[b0 + lane % 32]
+  // [h][16 ks + 8 kg .. +7]; the first block is loaded with the weights
+  u32x4 av[8];
+  auto load_q = [&](int b0) {
+    const int bb = b0 + (lane & 31);
+    const bool ok = bb < b_hi;
+    const uint16_t* qrow = q_nope + ((size_t)(ok ? bb : b_lo) * H + h) * kDN + 8 * kg;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) av[ks] = ok ? *(const u32x4*)(qrow + 16 * ks) : u32x4{0, 0, 0, 0};
+  };
+  load_q(b_lo);
   for (int i = tid; i < 128 * 16; i += 256) {
     const int r = i >> 4, ch = i & 15;
     *(u32x4*)&sW[r][8 * ch] = *(const u32x4*)(wkv_b + ((size_t)h * (kDN + kDV) + r) * kC + cblk * 128 + 8 * ch);
   }
   __syncthreads();
-  const int lane = tid & 63, wave = tid >> 6;
-  const int cc = 32 * wave + (lane & 31), kg = lane >> 5;
   u32x4 bw[8];  // B[k = d][n = c]: lane holds d = 16 ks + 8 kg + j of column cc
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
@@ -374,12 +385,7 @@ __global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict_
       bw[ks][j] = (uint32_t)sW[16 * ks + 8 * kg + 2 * j][cc] | ((uint32_t)sW[16 * ks + 8 * kg + 2 * j + 1][cc] << 16);
   }
   for (int b0 = b_lo; b0 < b_hi; b0 += 32) {
-    const int bb = b0 + (lane & 31);
-    const bool ok = bb < b_hi;
-    const uint16_t* qrow = q_nope + ((size_t)(ok ? bb : b_lo) * H + h) * kDN + 8 * kg;
-    u32x4 av[8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) av[ks] = ok ? *(const u32x4*)(qrow + 16 * ks) : u32x4{0, 0, 0, 0};
+    if (b0 != b_lo) load_q(b0);
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) acc = mfma32(av[ks], bw[ks], acc);
@@ -1283,7 +1289,7 @@ __global__ __launch_bounds__(64 * kCombineGroups) void combine_kernel(
   const float* pm = part_ml + (s0 * H + (hv ? h : 0)) * 2;
   const uint16_t* po = part_o + s0 * Hp * kC + (size_t)r * 512 + 8 * lane;
   const size_t ml_stride = (size_t)H * 2, o_stride = (size_t)Hp * kC;
-  __shared__ float sRed[kCombineGroups - 1][64][10];
+  extern __shared__ float sRed[];  // [NG - 1][64][10]: sized per launch
   Merge mg;
   auto unpack = [](const u32x4& v, float* f) {
 #pragma unroll
@@ -1318,7 +1324,7 @@ __global__ __launch_bounds__(64 * kCombineGroups) void combine_kernel(
     }
   }
   if (sg > 0) {
-    float* d = sRed[sg - 1][lane];
+    float* d = sRed + ((sg - 1) * 64 + lane) * 10;
 #pragma unroll
     for (int e = 0; e < 8; ++e) d[e] = mg.acc[e];
     d[8] = mg.M;
@@ -1327,7 +1333,7 @@ __global__ __launch_bounds__(64 * kCombineGroups) void combine_kernel(
   __syncthreads();
   if (sg == 0 && hv) {
     for (int k = 0; k < NG - 1; ++k) {
-      const float* d = sRed[k][lane];
+      const float* d = sRed + (k * 64 + lane) * 10;
       // a group's (acc, L) is already relative to 2^M_k: merge as a partial
       // with m = M_k, l = L_k and values acc_k / 1
       mg.add(d[8], d[9], d);
@@ -1453,7 +1459,8 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
   // average sequence (at most 256 partials are in use when B <= 256)
   const long long avg_parts = std::max<long long>(1, std::min<long long>(plan.max_groups, 256) / B);
   const int ng = avg_parts >= 32 ? 8 : (avg_parts >= 16 ? 4 : (avg_parts >= 8 ? 2 : 1));
-  err = launch_kernel(combine_kernel, dim3(B, plan.head_blocks * 32), dim3(64 * ng), stream, evk(2),
+  err = launch_kernel_lds(combine_kernel, dim3(B, plan.head_blocks * 32), dim3(64 * ng),
+                          (size_t)(ng - 1) * 64 * 10 * sizeof(float), stream, evk(2),
                       (const uint16_t*)part_o, (const float*)part_ml, (const int32_t*)wcum, olat, H,
                       plan.heads_padded);
   if (err != hipSuccess) return err;

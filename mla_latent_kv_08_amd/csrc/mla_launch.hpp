@@ -40,11 +40,16 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
 // dispatch are stamped into ev[0] and ev[1] by the dispatch itself (no extra
 // queue packets, so the elapsed time is the kernel's own duration).
 template <typename... KArgs, typename... Args>
+hipError_t launch_kernel_lds(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds_bytes,
+                             hipStream_t stream, hipEvent_t const* ev, Args... args) {
+  if (ev) hipExtLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, ev[0], ev[1], 0, args...);
+  else hipLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, args...);
+  return hipGetLastError();
+}
+template <typename... KArgs, typename... Args>
 hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
                          hipEvent_t const* ev, Args... args) {
-  if (ev) hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, ev[0], ev[1], 0, args...);
-  else hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
-  return hipGetLastError();
+  return launch_kernel_lds(kernel, grid, block, 0, stream, ev, args...);
 }
 hipError_t launch_cache_write(const mla_params& p, const CacheWriteArgs& c, hipStream_t stream);
 
