@@ -509,6 +509,26 @@ __device__ __forceinline__ void lds_dma4_after(const void* src, uint32_t base, u
                : "memory", "m0", "scc");
 }
 
+// The same copies addressed as a 64-bit scalar base plus a 32-bit per-lane
+// byte offset (no per-lane 64-bit address arithmetic).  The base must be
+// the same in every lane; it is moved to scalar registers explicitly.
+__device__ __forceinline__ uint64_t uniform64(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+template <int OFF>
+__device__ __forceinline__ void lds_dma16_s(uint64_t sbase, uint32_t voff, uint32_t base, uint32_t dep) {
+  asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(base), "i"(OFF), "v"(dep)
+               : "memory", "m0", "scc");
+}
+template <int OFF>
+__device__ __forceinline__ void lds_dma4_s(uint64_t sbase, uint32_t voff, uint32_t base, uint32_t dep) {
+  asm volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(base), "i"(OFF), "v"(dep)
+               : "memory", "m0", "scc");
+}
+
 // lds_dma16 issued after `dep` is available: when dep was read from the LDS
 // bytes this load overwrites, that read has completed first.
 template <int OFF>
@@ -776,16 +796,48 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     asm volatile("" : "+v"(ln));
     return ln;
   };
+  // Per-lane byte offsets of a dense tile of 32 selected rows, from its first
+  // row, packed two 16-bit values per register (computed once):
+  //   fo_a: codes of unit 0 (kv bytes) | bf16 rotary store (tile elements)
+  //   fo_b: scale (kv_scale bytes)     | rotary load (pe bytes)
+  //   fo_st[p]: bf16 stores of units p, p + 2 (tile elements), halves 0 | 1
+  uint32_t fo_a = 0u, fo_b = 0u, fo_st0 = 0u, fo_st1 = 0u;
+  // unpacked at each use (hoisted per-slot addresses would not fit)
+  auto fresh = [](uint32_t v) MLA_INLINE -> uint32_t {
+    asm volatile("" : "+v"(v));
+    return v;
+  };
+  if (FP8) {  // (with top-k only the rotary store offset is used)
+    const int x = lane >> 3, c = lane & 7;
+    fo_a = (uint32_t)(x * kC + kBlk * wave + 16 * c) | ((uint32_t)tile_off(8 * wave + x, 64 + c) << 16);
+    if (!TOPK)
+      fo_b = (uint32_t)(16 * (8 * (lane & 3) + (lane >> 2)) + 4 * wave) | ((uint32_t)((8 * wave + x) * kR * 2 + 16 * c) << 16);
+    fo_st0 = (uint32_t)tile_off(x, 16 * wave + 2 * c) | ((uint32_t)tile_off(x, 16 * wave + 2 * c + 1) << 16);
+    fo_st1 = (uint32_t)tile_off(8 + x, 16 * wave + 2 * c) | ((uint32_t)tile_off(8 + x, 16 * wave + 2 * c + 1) << 16);
+  }
   // Load n of a raw tile (issue order, which the conversion's waits count
   // on): 0 scales, 1..4 code units 0..3, 5 rotary rows.  `dep`: a value read
   // from the bytes this load replaces (orders the load after that read).
-  // A dense tile of 32 selected rows takes fixed offsets from its first row.
+  // A dense tile of 32 selected rows takes the fixed offsets above from its
+  // first row (scalar base); any other tile computes each lane's row.
   auto fp8_load = [&](int j, auto N, uint32_t dep = 0u) MLA_INLINE {
     constexpr int n = decltype(N)::value;
     const int pt = p0 + j * kTT;
     const bool full = !TOPK && pt + kTT <= p1;
     uint32_t base = lds_addr(fregion);
     asm volatile("" : "+s"(base));
+    if (full) {
+      const size_t r0 = seq_row0 + pt;
+      if constexpr (n >= 1 && n <= 4) {
+        constexpr int u = n - 1;
+        lds_dma16_s<1024 * u>(uniform64((const uint8_t*)a.kv + r0 * kC + 4096 * u), fresh(fo_a) & 0xFFFFu, base, dep);
+      } else if constexpr (n == 0) {
+        if (lane < 32) lds_dma4_s<kFp8WaveCodes>(uniform64(a.kv_scale + r0 * 4), fresh(fo_b) & 0xFFFFu, base, dep);
+      } else {
+        lds_dma16_s<kFp8WaveCodes + kFp8WaveScales>(uniform64(a.pe + r0 * kR), fresh(fo_b) >> 16, base, dep);
+      }
+      return;
+    }
     const int ln = fresh_lane();
     if constexpr (n >= 1 && n <= 4) {
       constexpr int u = n - 1;
@@ -824,10 +876,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)q, true);
     return u32x2{cvt_pk_bf16(lo[0] * sc, lo[1] * sc), cvt_pk_bf16(hi[0] * sc, hi[1] * sc)};
   };
-  // store half `c` (8 values) of unit u of this lane into the tile
+  // store half `c` (8 values) of unit u of this lane into the tile: units u
+  // and u + 2 share the swizzle (rows 8u + l/8 and 8u + 16 + l/8)
   auto fp8_store = [&](uint16_t* dst, auto U, int c, const u32x4& w) MLA_INLINE {
-    const int ln = fresh_lane();
-    *(u32x4*)(dst + tile_off(8 * decltype(U)::value + (ln >> 3), 16 * wave + 2 * (ln & 7) + c)) = w;
+    constexpr int u = decltype(U)::value;
+    const uint32_t pk = fresh((u & 1) ? fo_st1 : fo_st0);
+    const uint32_t off = c ? (pk >> 16) : (pk & 0xFFFFu);
+    *(u32x4*)(dst + off + (u >> 1) * 16 * kQK) = w;
   };
   auto fp8_write = [&](uint16_t* dst, auto U, const u32x4& q, float sc) MLA_INLINE {
     const u32x2 a = fp8_cvt4(q[0], sc), b = fp8_cvt4(q[1], sc);
@@ -839,8 +894,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     return *(const u32x4*)(fregion + kFp8WaveCodes + kFp8WaveScales + 16 * fresh_lane());
   };
   auto fp8_rope_write = [&](uint16_t* dst, const u32x4& v) MLA_INLINE {
-    const int ln = fresh_lane();
-    *(u32x4*)(dst + tile_off(8 * wave + (ln >> 3), 64 + (ln & 7))) = v;
+    *(u32x4*)(dst + (fresh(fo_a) >> 16)) = v;
   };
   auto fp8_rope = [&](uint16_t* dst) MLA_INLINE { fp8_rope_write(dst, fp8_rope_read()); };
   // the whole conversion of tile j into slot S in one go (prologue, and waves
