@@ -388,3 +388,53 @@ def test_multitoken_decode_step(m, fp8):
     m.cache_write(to_dev(kv_new), to_dev(pe_new), to_dev((lens - s).to(torch.int32)), kv2, pe2, kv_scale=sc2)
     out2 = m.decode(*args, kv2, pe2, to_dev(lens), kv_scale=sc2)
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+# ---------------------------------------------------------------- HIP graph capture
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_decode_step_graph_replays(m, fp8):
+    """The fused step recorded into a HIP graph gives, on every replay, the eager
+    result bit for bit (the header promises capture safety; the benchmark relies on it)."""
+    w = synth.Workload("graph", 4, 128, 700, fp8=fp8, ragged=(1, 700), seed=61)
+    x = synth.make_inputs(w)
+    kv_h, sc_h, pe_h = _upload_caches(m, w, x)
+    lens = x["cache_lens"]
+    B, T = w.batch, w.max_seq_len
+    # the new row of every sequence is the row already cached there, so the
+    # step leaves the caches as they are and every call sees the same inputs
+    rows = (lens.long() - 1).clamp(min=0)
+    kv_new = x["kv"][torch.arange(B), rows].reshape(B, 1, 512).contiguous()
+    pe_new = x["pe"][torch.arange(B), rows].reshape(B, 1, 64).contiguous()
+    if fp8:  # FP8: the re-quantised row must reproduce its stored codes
+        codes, scales, _ = oracle.cache_write(kv_new, pe_new, (lens - 1).to(torch.int32), T, True,
+                                              kv_cache=kv_h.numpy().copy(), kv_scale=sc_h.numpy().copy(),
+                                              pe_cache=pe_h.view(torch.int16).numpy().view(np.uint16).copy())
+        assert np.array_equal(codes, kv_h.numpy()) and np.array_equal(scales.view(np.uint32), sc_h.numpy().view(np.uint32))
+    d = {k: to_dev(v) for k, v in dict(q_nope=x["q_nope"], q_pe=x["q_pe"], wkv_b=x["wkv_b"], kv=kv_h, sc=sc_h,
+                                        pe=pe_h, lens=lens, kv_new=kv_new, pe_new=pe_new).items()}
+    p = m.make_params(B, w.heads, T, 1 if fp8 else 0)
+    ws = torch.empty(m.decode_workspace_size(p), dtype=torch.uint8, device=DEV)
+    out = torch.empty(B, 1, w.heads, 128, dtype=torch.bfloat16, device=DEV)
+    step = lambda: m.decode_step(d["kv_new"], d["pe_new"], d["q_nope"], d["q_pe"], d["wkv_b"], d["kv"], d["pe"],
+                                 d["lens"], kv_scale=d["sc"], out=out, workspace=ws)
+    print(f"[graph] fp8={fp8}", flush=True)
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        out.fill_(-1.0)          # eager work between the replays
+        ws.fill_(0x7F)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r} differs"
