@@ -1132,11 +1132,22 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     // into its slot during the score MFMAs, then the raw tile j+2 is loaded
     // into the staging region (its own reads of it done).
     const bool fast = !FP8 && !TOPK && j + 1 < ntiles && p0 + (j + 2) * kTT <= p1;
+    // top-k: the gathered tile j+1 is loaded one load per group of score
+    // MFMAs too (each load looks its row up in the staged indices)
+    const bool gather = !FP8 && TOPK && j + 1 < ntiles;
     const bool fp8_cv = FP8 && j + 1 < ntiles, fp8_ld = FP8 && j + 2 < ntiles;
     const FullTile ft = full_tile(j + 1, Stage<s1>{});
     if (!FP8 && j + 1 < ntiles) {
-      if (fast) publish_mask(p0 + (j + 1) * kTT, s1);
+      if (fast || gather) publish_mask(p0 + (j + 1) * kTT, s1);
       else issue_bf16(j + 1, Stage<s1>{});
+    }
+    DmaCursor gc{0, 0};
+    uint32_t gbase = 0u;
+    if constexpr (TOPK && !FP8) {
+      if (gather) {
+        gc = dma_start();
+        gbase = dma_base(slot(Stage<s1>{}));
+      }
     }
     if (tid == 0) sRescale[(j + 1) % 3] = 0u;  // flag of tile j-2: read in body j-1
     const uint16_t* tile = slot(S);
@@ -1169,6 +1180,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
           asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(s) : "v"(ka[k % (kScoreAhead + 1)]), "v"(qreg[k]));
         if constexpr (kk == 1) {
           if (fast) full_load(ft, Q);
+          if constexpr (TOPK && !FP8) {
+            if (gather) dma_step(gc, p0 + (j + 1) * kTT, gbase, Q);
+          }
         }
         if constexpr (FP8) {
           // conversion of tile j+1, one dword of codes per MFMA (the VALU work
@@ -1236,6 +1250,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
       group(Stage<8>{});
     } else if (fast) {
       full_all(ft);
+    } else if (gather) {
+      dma_all(gc, p0 + (j + 1) * kTT, gbase);
     } else if (FP8) {
       if (fp8_cv) {
         MLA_WAIT_VMCNT(0);
