@@ -475,6 +475,7 @@ struct AttnArgs {
   uint16_t* part_o;       // [grid][H][512]
   float* part_ml;         // [grid][H][2]
   int B, s, H, Hp, T, topk, head_blocks;  // B: query tokens (batch x s)
+  int head_split;  // workgroups per plan workgroup, each with head_blocks / head_split blocks
   float scale_log2;
 };
 
@@ -563,7 +564,12 @@ struct Stage {
 
 template <bool FP8, bool TOPK>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
-  const int grp = blockIdx.x;
+  // Workgroup x runs head group hq (of HS) of plan workgroup grp; the HS
+  // workgroups of one plan workgroup sit on its XCD (x % 8 == grp % 8) and
+  // share its tiles in that XCD's L2.
+  const int HS = a.head_split, x = blockIdx.x;
+  const int grp = (x / (8 * HS)) * 8 + (x & 7), hq = (x >> 3) % HS;
+  const int nhb = a.head_blocks / HS, hb0 = hq * nhb;  // this workgroup's head blocks
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int4 rec = a.rec[grp];
@@ -597,9 +603,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     else return sT2;
   };
 
-  const bool active = wave < a.head_blocks;  // this wave has score heads
+  const bool active = wave < nhb;  // this wave has score heads
   const int n = lane & 31, g = lane >> 5;
-  const int head = wave * 32 + n;
+  const int head = wave * 32 + n;           // in this workgroup (P rows, alpha)
+  const int ghead = (hb0 + wave) * 32 + n;  // in the layer
 
   // P rows and l of heads without a score wave stay zero; their alpha stays 1.
   for (int i = tid; i < 2 * 128 * kPStride / 2; i += kAttnThreads) ((uint32_t*)sP)[i] = 0u;
@@ -932,7 +939,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   // absorb kernel: one 1 KB row per wave and k-step).
   u32x4 qreg[36];
   if (active) {
-    const u32x4* src = (const u32x4*)(a.qt + ((size_t)b * a.head_blocks + wave) * (36 * 512)) + lane;
+    const u32x4* src = (const u32x4*)(a.qt + ((size_t)b * a.head_blocks + hb0 + wave) * (36 * 512)) + lane;
 #pragma unroll
     for (int st = 0; st < 36; ++st) qreg[st] = src[64 * st];
   }
@@ -1289,12 +1296,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   // holds O[head 32 nb + lane % 32][128 wave + 32 m + 16 q2 + 8 (j / 4)
   // + 4 (lane / 32) + j % 4] at position j, one 1 KB row per store.
   const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  if (active && g == 0 && head < a.H) {
-    float* pm = a.part_ml + (slot_id * a.H + head) * 2;
+  if (active && g == 0 && ghead < a.H) {
+    float* pm = a.part_ml + (slot_id * a.H + ghead) * 2;
     pm[0] = l_tot > 0.f ? m_run : -INFINITY;
     pm[1] = l_tot;
   }
-  uint16_t* dst = a.part_o + slot_id * (size_t)a.Hp * kC + (size_t)wave * (8 * 512) + 8 * lane;
+  uint16_t* dst = a.part_o + slot_id * (size_t)a.Hp * kC + (size_t)hb0 * (32 * 512) + (size_t)wave * (8 * 512) + 8 * lane;
   auto store_block = [&](auto NB) MLA_INLINE {
     constexpr int nb = decltype(NB)::value;
 #pragma unroll
@@ -1308,9 +1315,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     }
   };
   store_block(Stage<0>{});
-  if (a.head_blocks > 1) store_block(Stage<1>{});
-  if (a.head_blocks > 2) store_block(Stage<2>{});
-  if (a.head_blocks > 3) store_block(Stage<3>{});
+  if (nhb > 1) store_block(Stage<1>{});
+  if (nhb > 2) store_block(Stage<2>{});
+  if (nhb > 3) store_block(Stage<3>{});
 }
 
 // ---------------------------------------------------------------------------
@@ -1518,8 +1525,9 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
   aa.T = p.max_seq_len;
   aa.topk = p.topk;
   aa.head_blocks = plan.head_blocks;
+  aa.head_split = plan.head_split;
   aa.scale_log2 = p.softmax_scale * 1.4426950408889634f;
-  const dim3 agrid((unsigned)plan.max_groups);
+  const dim3 agrid((unsigned)(plan.max_groups * plan.head_split));
   auto attn = fp8 ? (topk ? attn_kernel<true, true> : attn_kernel<true, false>)
                   : (topk ? attn_kernel<false, true> : attn_kernel<false, false>);
   err = launch_kernel(attn, agrid, dim3(kAttnThreads), stream, evk(1), aa);

@@ -29,6 +29,8 @@ constexpr int kMaxTopkGroupTiles = 32;  // top-k: tiles per workgroup (index sta
 struct DecodePlan {
   int heads_padded;     // H rounded up to a multiple of 32 (one 32-head block per wave)
   int head_blocks;      // heads_padded / 32
+  int head_split;       // attention workgroups per plan workgroup (1, 2 or 4), each
+                        // with head_blocks / head_split of the head blocks
   long long max_groups; // attention grid (upper bound of sum k_b)
   int min_group_tiles;  // lower bound of S
   long long max_tiles;  // tiles of the longest possible selection
@@ -52,7 +54,19 @@ inline DecodePlan make_decode_plan(const mla_params& p) {
     const long long capped = (long long)B * ((d.max_tiles + kMaxTopkGroupTiles - 1) / kMaxTopkGroupTiles);
     if (G < capped) G = capped;
   }
+  // no sequence takes more than ceil(max_tiles / min_group_tiles) workgroups
+  const long long bound = (long long)B * ((d.max_tiles + d.min_group_tiles - 1) / d.min_group_tiles);
+  if (G > bound) G = bound;
+  G = (G + 7) / 8 * 8;  // whole rows of the XCD placement
   d.max_groups = G;
+  // Few workgroups (a short batch): split each one's heads over up to four
+  // workgroups, so that more CUs load the query and share the tile loads.
+  // Each CU keeps only a limited amount of loads in flight, and every
+  // workgroup of a token loads the whole absorbed query (144 KB at 128 heads).
+  d.head_split = 1;
+  while (d.head_split < 4 && d.head_blocks % (2 * d.head_split) == 0 &&
+         G * 2 * d.head_split <= kTargetCUs)
+    d.head_split *= 2;
   size_t off = 0;
   d.off_qt = off;  // bf16 [B tokens][heads_padded][576], in the attention kernel's fragment order
   off = align256(off + (size_t)B * d.heads_padded * 576 * 2);
