@@ -319,7 +319,7 @@ __device__ __forceinline__ void write_new_rows(const RowWrite& rw, const int32_t
 // contiguous per wave.  Padded heads are zero.
 // ---------------------------------------------------------------------------
 template <int WRITE>
-__global__ __launch_bounds__(256) void absorb_kernel(const uint16_t* __restrict__ q_nope,
+__global__ __launch_bounds__(256, 3) void absorb_kernel(const uint16_t* __restrict__ q_nope,
                                                      const uint16_t* __restrict__ q_pe,
                                                      const uint16_t* __restrict__ wkv_b,
                                                      uint16_t* __restrict__ qt, int B, int s, int H,
