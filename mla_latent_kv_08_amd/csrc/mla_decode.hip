@@ -562,7 +562,10 @@ struct Stage {
   static constexpr int value = S;
 };
 
-template <bool FP8, bool TOPK>
+// NHB: head blocks per workgroup the update keeps accumulators for (4; or the
+// workgroup's exact count 1 or 2 when it has that few: no MFMAs on blocks
+// whose probabilities would all be zero).
+template <bool FP8, bool TOPK, int NHB>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   // Workgroup x runs head group hq (of HS) of plan workgroup grp; the HS
   // workgroups of one plan workgroup sit on its XCD (x % 8 == grp % 8) and
@@ -919,15 +922,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     publish_mask(p0 + j * kTT, decltype(S)::value);
   };
 
-  // O accumulators o[4 * m + nb]: columns 128w + 32m + ..., heads 32nb + ...
+  // O accumulators o[NHB m + nb]: columns 128w + 32m + ..., heads 32nb + ...
   // Every definition of o[] is an MFMA result (zero operands for the initial
   // value and in the rescale below): a VALU definition would make the
   // compiler keep the loop-carried accumulators in VGPRs and copy them every
   // iteration.
   const u32x4 zq = {0u, 0u, 0u, 0u};
-  f32x16 o[16];
+  f32x16 o[4 * NHB];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) o[i] = mfma32(zq, zq, f32x16{});
+  for (int i = 0; i < 4 * NHB; ++i) o[i] = mfma32(zq, zq, f32x16{});
   float m_run = -INFINITY, l_run = 0.f;
 
   // ---- pipeline prologue: the first tiles and the query are loaded
@@ -962,14 +965,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   auto rescale = [&](int jj) MLA_INLINE {
     if (sRescale[(jj + 3) % 3]) {  // rare: some head's running max moved
       const float* al_src = sAlpha + (jj & 1) * 128;
-      float al[4];
+      float al[NHB];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) al[nb] = al_src[32 * nb + n];
+      for (int nb = 0; nb < NHB; ++nb) al[nb] = al_src[32 * nb + n];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
+      for (int i = 0; i < 4 * NHB; ++i) {
         f32x16 tcopy = o[i];
         asm volatile("" : "+v"(tcopy));  // scale a copy; o[i] itself stays an MFMA value
-        o[i] = mfma32(zq, zq, tcopy * al[i & 3]);
+        o[i] = mfma32(zq, zq, tcopy * al[i % NHB]);
       }
     }
   };
@@ -981,13 +984,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     const u32x2 v1 = ds_read_tr16(base + tr_base[1][m & 1]);
     return u32x4{v0[0], v0[1], v1[0], v1[1]};
   };
-  auto pv_mfma_any = [&](const u32x4& va, const u32x4 (&pb)[4], int m) MLA_INLINE {
+  auto pv_mfma_any = [&](const u32x4& va, const u32x4 (&pb)[NHB], int m) MLA_INLINE {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) o[4 * m + nb] = mfma32(va, pb[nb], o[4 * m + nb]);
+    for (int nb = 0; nb < NHB; ++nb) o[NHB * m + nb] = mfma32(va, pb[nb], o[NHB * m + nb]);
   };
-  auto pb_read_any = [&](const uint16_t* pp, u32x4 (&pb)[4], int u) MLA_INLINE {
+  auto pb_read_any = [&](const uint16_t* pp, u32x4 (&pb)[NHB], int u) MLA_INLINE {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) pb[nb] = *(const u32x4*)(pp + (32 * nb + n) * kPStride + 16 * u + 8 * g);
+    for (int nb = 0; nb < NHB; ++nb) pb[nb] = *(const u32x4*)(pp + (32 * nb + n) * kPStride + 16 * u + 8 * g);
   };
   // Update with tile jp interleaved with the softmax of tile j held in s:
   // eight scheduling regions, each with the four MFMAs of one update step
@@ -1002,7 +1005,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     auto interleave = [&]() MLA_INLINE {
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
+      for (int r = 0; r < NHB; ++r) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
       }
@@ -1010,16 +1013,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
       __builtin_amdgcn_sched_group_barrier(0x200, 8, 0);
     };
     const uint16_t* pp = pbuf(jp);
-    u32x4 pb[4], va[4];
+    u32x4 pb[NHB], va[4];
     float mx, m_use, m_sub, alpha;
     auto tr_read = [&](const uint16_t* pt, int u, int m) MLA_INLINE -> u32x4 {
       if constexpr (pv) return tr_read_any(pt, u, m);
       else return u32x4{0u, 0u, 0u, 0u};
     };
-    auto pv_mfma = [&](const u32x4& va, const u32x4(&pb)[4], int m) MLA_INLINE {
+    auto pv_mfma = [&](const u32x4& va, const u32x4(&pb)[NHB], int m) MLA_INLINE {
       if constexpr (pv) pv_mfma_any(va, pb, m);
     };
-    auto pb_read = [&](const uint16_t* pp, u32x4(&pb)[4], int u) MLA_INLINE {
+    auto pb_read = [&](const uint16_t* pp, u32x4(&pb)[NHB], int u) MLA_INLINE {
       if constexpr (pv) pb_read_any(pp, pb, u);
     };
     pb_read(pp, pb, 0);
@@ -1113,7 +1116,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   // The update alone (after the last tile).
   auto update_only = [&](const uint16_t* ptile, int jp) MLA_INLINE {
     const uint16_t* pp = pbuf(jp);
-    u32x4 pb[4];
+    u32x4 pb[NHB];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       pb_read_any(pp, pb, u);
@@ -1306,7 +1309,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     constexpr int nb = decltype(NB)::value;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      const f32x16& ob = o[4 * m + nb];
+      const f32x16& ob = o[NHB * m + nb];
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2)
         *(u32x4*)(dst + (size_t)nb * (32 * 512) + (2 * m + q2) * 512) =
@@ -1315,9 +1318,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     }
   };
   store_block(Stage<0>{});
-  if (nhb > 1) store_block(Stage<1>{});
-  if (nhb > 2) store_block(Stage<2>{});
-  if (nhb > 3) store_block(Stage<3>{});
+  if constexpr (NHB > 1) {
+    if (nhb > 1) store_block(Stage<1>{});
+  }
+  if constexpr (NHB > 3) {
+    if (nhb > 2) store_block(Stage<2>{});
+    if (nhb > 3) store_block(Stage<3>{});
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1528,8 +1535,11 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
   aa.head_split = plan.head_split;
   aa.scale_log2 = p.softmax_scale * 1.4426950408889634f;
   const dim3 agrid((unsigned)(plan.max_groups * plan.head_split));
-  auto attn = fp8 ? (topk ? attn_kernel<true, true> : attn_kernel<true, false>)
-                  : (topk ? attn_kernel<false, true> : attn_kernel<false, false>);
+  // bf16 workgroups with one or two head blocks get their own accumulator count
+  const int nhb = plan.head_blocks / plan.head_split;
+  auto attn = fp8 ? (topk ? attn_kernel<true, true, 4> : attn_kernel<true, false, 4>)
+                  : (topk ? (nhb == 1 ? attn_kernel<false, true, 1> : nhb == 2 ? attn_kernel<false, true, 2> : attn_kernel<false, true, 4>)
+                          : (nhb == 1 ? attn_kernel<false, false, 1> : nhb == 2 ? attn_kernel<false, false, 2> : attn_kernel<false, false, 4>));
   err = launch_kernel(attn, agrid, dim3(kAttnThreads), stream, evk(1), aa);
   if (err != hipSuccess) return err;
 

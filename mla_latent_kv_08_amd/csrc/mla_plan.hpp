@@ -48,7 +48,7 @@ inline DecodePlan make_decode_plan(const mla_params& p) {
   d.head_blocks = d.heads_padded / 32;
   const long long n_max = p.topk > 0 ? p.topk : p.max_seq_len;
   d.max_tiles = (n_max + kTileRows - 1) / kTileRows;
-  d.min_group_tiles = 2;
+  d.min_group_tiles = p.topk > 0 ? 4 : 2;
   long long G = B > kTargetCUs ? B : kTargetCUs;
   if (p.topk > 0) {
     const long long capped = (long long)B * ((d.max_tiles + kMaxTopkGroupTiles - 1) / kMaxTopkGroupTiles);
