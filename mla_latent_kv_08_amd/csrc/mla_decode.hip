@@ -1443,6 +1443,18 @@ __global__ __launch_bounds__(64) void uproj_kernel(const uint16_t* __restrict__ 
                                                    uint16_t* __restrict__ out, int B, int H) {
   const int h = blockIdx.x, d0 = 32 * blockIdx.y;
   const int lane = threadIdx.x, r = lane & 15, g = lane >> 4;
+  // A operand of the block of sequences b0 .. b0 + 15: lane holds o[b0 + r][h][32 ks + 8 g .. +7]
+  auto load_a = [&](int b0, u32x4 (&av)[16]) {
+    const int bb = b0 + r;
+    const bool bok = bb < B;
+    const uint16_t* arow = olat + ((size_t)(bok ? bb : 0) * H + h) * kC + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) av[ks] = bok ? *(const u32x4*)(arow + 32 * ks) : u32x4{0, 0, 0, 0};
+  };
+  // the first block's rows go out with the weights, and each next block's
+  // before the current block's MFMAs, so only one load latency is exposed
+  u32x4 av[16], an[16];
+  load_a(0, av);
   const uint16_t* w0 = wkv_b + ((size_t)h * (kDN + kDV) + kDN + d0 + r) * kC + 8 * g;
   const uint16_t* w1 = w0 + (size_t)16 * kC;
   u32x4 bw0[16], bw1[16];
@@ -1452,12 +1464,7 @@ __global__ __launch_bounds__(64) void uproj_kernel(const uint16_t* __restrict__ 
     bw1[ks] = *(const u32x4*)(w1 + 32 * ks);
   }
   for (int b0 = 0; b0 < B; b0 += 16) {
-    const int bb = b0 + r;
-    const bool bok = bb < B;
-    const uint16_t* arow = olat + ((size_t)(bok ? bb : 0) * H + h) * kC + 8 * g;
-    u32x4 av[16];
-#pragma unroll
-    for (int ks = 0; ks < 16; ++ks) av[ks] = bok ? *(const u32x4*)(arow + 32 * ks) : u32x4{0, 0, 0, 0};
+    if (b0 + 16 < B) load_a(b0 + 16, an);
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
@@ -1473,6 +1480,8 @@ __global__ __launch_bounds__(64) void uproj_kernel(const uint16_t* __restrict__ 
         dst[16] = (uint16_t)f2bf(acc1[j]);
       }
     }
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) av[ks] = an[ks];
   }
 }
 
