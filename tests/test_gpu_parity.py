@@ -92,8 +92,12 @@ def run_case(m, w, x, pairs=None, label=""):
 
 # ---------------------------------------------------------------- small cases, full compare
 
+# The attention grid depends on the plan: B=1 T=8192 at H=128 (128 plan
+# workgroups) splits each one's heads over two workgroups of two head blocks;
+# B=4 T=4096 at H=64 (256) runs unsplit workgroups of two head blocks; the
+# short cases split four ways into single head blocks.
 @pytest.mark.parametrize("B,H,T", [(1, 16, 256), (2, 128, 300), (3, 48, 97), (1, 100, 33),
-                                   (2, 32, 1), (1, 128, 64)])
+                                   (2, 32, 1), (1, 128, 64), (1, 128, 8192), (4, 64, 4096)])
 def test_dense_small(m, B, H, T):
     w = synth.Workload("dense", B, H, T, seed=100 + T)
     run_case(m, w, synth.make_inputs(w), label=f"dense B{B} H{H} T{T}")
