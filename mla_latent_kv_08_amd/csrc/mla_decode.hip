@@ -409,35 +409,40 @@ __global__ __launch_bounds__(256, 3) void absorb_kernel(const uint16_t* __restri
 // ---------------------------------------------------------------------------
 // attention (split-T flash decoding over a balanced tile split)
 //
-// grid: the workgroups of the plan (one round of at most one per CU in the
-// usual case), 256 threads = 4 waves (one per SIMD).  Workgroup i handles a
-// run of tiles of one sequence (see make_decode_plan) and writes its partial
-// (O / l, m, l) into slot i.  Its tiles (32 cache rows in LDS, row-major
-// [t][576]: 512 latent then 64 rotary values) stream through a ring of
-// kStages tiles.  Per tile:
-//   1. scores: wave w owns heads 32w..32w+31.  S^T[t][h] = K[t][:] . Qa[h][:]
-//      with 36 MFMA 32x32x16 (A: 16-byte row reads of the tile, B: the wave's
-//      Qa in 144 registers).  Lane l holds head l%32, rows 8(e/4)+4(l/32)+e%4.
+// grid: the plan's workgroups (at most one per CU, one round in the usual
+// case) times the head split HS (1, 2 or 4: a short plan's workgroups are
+// split by head blocks so that more CUs share its fixed loads), 256 threads
+// = 4 waves (one per SIMD).  Plan workgroup i handles a run of tiles of one
+// query token (see make_decode_plan) and its HS workgroups write the
+// unnormalised partial O with (m, l) into plan slot slot_of[i].  Its tiles
+// (32 cache rows in LDS, row-major [t][576]: 512 latent then 64 rotary
+// values) stream through a ring of kStages tiles.  Per tile:
+//   1. scores: wave w owns the workgroup's head block w (heads
+//      32 (hb0 + w) .. +31; waves past the workgroup's blocks only run the
+//      update).  S^T[t][h] = K[t][:] . Qa[h][:] with 36 MFMA 32x32x16 (A:
+//      16-byte row reads of the tile, B: the wave's Qa in 144 registers).
+//      Lane l holds head l%32, rows 8(e/4)+4(l/32)+e%4.
 //   2. online softmax of those heads (the other 16 rows of a head sit in lane
 //      l^32); P (bf16) goes to sP[head][tau], tau = row with bits 2 and 3
 //      swapped, which makes each lane's 8 consecutive P values contiguous.
 //   3. update, split by latent columns: wave w owns O^T[c][h] for c in
-//      128w..128w+127 and all 128 heads (16 accumulator blocks, 256 AGPRs).
-//      O^T += V^T . P^T with A = V^T from ds_read_tr16_b64 transposing reads
-//      of the tile (each read feeds 4 head blocks) and B = P^T from sP.
+//      128w..128w+127 and the workgroup's NHB head blocks (4 NHB accumulator
+//      blocks; 256 AGPRs at NHB = 4).  O^T += V^T . P^T with A = V^T from
+//      ds_read_tr16_b64 transposing reads of the tile (each read feeds NHB
+//      head blocks) and B = P^T from sP.
 // Splitting the update by columns keeps the LDS bytes per MFMA low: per tile
 // and workgroup 144 KB of score-operand reads, 32 KB of transposing reads and
-// 40 KB of P traffic.  At the end the normalised O is staged in the idle ring
-// as bf16 rows and written out as whole 1 KB rows per head.
+// 40 KB of P traffic.  At the end each lane's accumulators leave as bf16
+// straight to the partial in fragment order (1 KB per store and wave).
 //
 // bf16 cache: tile j+1 is copied global -> LDS directly (no registers) while
 // tile j is processed, its nine loads per thread spread over the score MFMAs.
 // One tile in flight per workgroup keeps the loads from ever waiting for
 // queue space (a second queued tile makes the issuing wave stall until the
-// first lands), and with one workgroup per CU it sustains most of the HBM
-// bandwidth.  FP8 cache: codes and scales of tile j+1 go through registers
-// and are dequantised to bf16(float(code) * scale) when written to LDS after
-// the update.
+// first lands).  FP8 cache: each wave stages its part of tile j+2 (codes,
+// scales, rotary rows) in its own LDS region by direct loads, and converts
+// its part of tile j+1 to bf16(float(code) * scale) inside the score chain
+// of tile j.
 //
 // LDS swizzle: logical 16-byte chunk ch of row t sits at chunk ch ^ F(t),
 // F(t) = 4((t>>1)&1) + ((t>>2)&3), which only permutes chunks inside their
