@@ -22,8 +22,9 @@ constexpr int kMaxTopkGroupTiles = 32;  // top-k: tiles per workgroup (index sta
 // tiles [floor(p t_b / k_b), floor((p+1) t_b / k_b)) and writes its partial
 // (O, m, l) into slot i.  S is the smallest budget with sum k_b <= 256 (one
 // round), at least min_group_tiles (2: a workgroup's fixed costs, the query
-// load and the 128 KB partial, then cover at least two tiles), and at most 32
-// with a top-k selection.
+// load and the 128 KB partial, then cover at least two tiles; 4 with a top-k
+// selection, whose gathered tiles are cheap next to the partial), and at most
+// 32 with a top-k selection.
 // The lengths live on the device, so w_b and S are computed there; the sizes
 // here are upper bounds.
 struct DecodePlan {
@@ -31,7 +32,8 @@ struct DecodePlan {
   int head_blocks;      // heads_padded / 32
   int head_split;       // attention workgroups per plan workgroup (1, 2 or 4), each
                         // with head_blocks / head_split of the head blocks
-  long long max_groups; // attention grid (upper bound of sum k_b)
+  long long max_groups; // plan workgroups (upper bound of sum k_b; the attention grid is
+                        // max_groups x head_split)
   int min_group_tiles;  // lower bound of S
   long long max_tiles;  // tiles of the longest possible selection
   size_t off_qt, off_part_o, off_part_ml, off_olat, off_wcum, off_rec, off_slot, bytes;
