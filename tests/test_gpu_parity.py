@@ -347,6 +347,38 @@ def test_multitoken_decode(m, B, s, H, T, fp8, topk):
         assert (out[2, 0].float() == 0).all()
 
 
+def _sweep_configs(n=20, seed=2026):
+    """Deterministic draw of small shapes over every plan path: batch, query
+    tokens, head count (whole, padded and odd head blocks, so the head split
+    and the one-, two- and four-block attention instances), ragged lengths,
+    top-k or dense, bf16 or FP8."""
+    rng = np.random.default_rng(seed)
+    cfgs = []
+    while len(cfgs) < n:
+        B = int(rng.integers(1, 7))
+        s = int(rng.choice([1, 1, 2, 3]))
+        H = int(rng.choice([16, 32, 48, 64, 96, 100, 128]))
+        T = int(rng.integers(s, 1500))
+        fp8 = bool(rng.random() < 0.3)
+        topk = int(rng.integers(1, T + 1)) if rng.random() < 0.3 else 0
+        if B * s * H * T <= 1_500_000:
+            cfgs.append((B, s, H, T, fp8, topk))
+    return cfgs
+
+
+@pytest.mark.parametrize("B,s,H,T,fp8,topk", _sweep_configs())
+def test_sweep_random_shapes(m, B, s, H, T, fp8, topk):
+    x = multitoken_case(B, s, H, T, fp8, topk, seed=7 * B + 11 * s + H + T)
+    kv, sc, pe = host_caches(x, T, fp8)
+    print(f"[sweep] B={B} s={s} H={H} T={T} fp8={fp8} topk={topk}", flush=True)
+    out = m.decode(to_dev(x["q_nope"]), to_dev(x["q_pe"]), to_dev(x["wkv_b"]), to_dev(kv), to_dev(pe),
+                   to_dev(x["cache_lens"]), kv_scale=to_dev(sc), topk_idx=to_dev(x["topk_idx"]))
+    torch.cuda.synchronize()
+    ref = oracle.decode(x["q_nope"], x["q_pe"], x["wkv_b"], kv, pe, x["cache_lens"], synth.SOFTMAX_SCALE,
+                        kv_scale=None if sc is None else sc.numpy(), topk_idx=x["topk_idx"])
+    check(out, ref, fp8, f"sweep B{B} s{s} H{H} T{T} fp8={fp8} topk={topk}")
+
+
 def test_multitoken_full_size_sampled(m):
     B, s, H, T = 4, 2, 128, 4096
     x = multitoken_case(B, s, H, T, False, 0, seed=41)
