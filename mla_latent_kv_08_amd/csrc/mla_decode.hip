@@ -441,8 +441,8 @@ __global__ __launch_bounds__(256, 3) void absorb_kernel(const uint16_t* __restri
 // queue space (a second queued tile makes the issuing wave stall until the
 // first lands).  FP8 cache: each wave stages its part of tile j+2 (codes,
 // scales, rotary rows) in its own LDS region by direct loads, and converts
-// its part of tile j+1 to bf16(float(code) * scale) inside the score chain
-// of tile j.
+// its part of tile j+1 to bf16(float(code) * scale) in one pass before the
+// score chain of tile j.
 //
 // LDS swizzle: logical 16-byte chunk ch of row t sits at chunk ch ^ F(t),
 // F(t) = 4((t>>1)&1) + ((t>>2)&3), which only permutes chunks inside their
@@ -1167,9 +1167,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     if (tid == 0) sRescale[(j + 1) % 3] = 0u;  // flag of tile j-2: read in body j-1
     const uint16_t* tile = slot(S);
     f32x16 s = {};  // waves without score heads run the softmax on zeros
-    u32x4 fq;       // FP8: staged codes of one unit
-    u32x2 fw;       // and the first bf16 pair of the half being converted
-    f32x4 fsc = {};  // and the scales of its four rows
+    // FP8: this wave's part of tile j+1 (staged during tile j-1) is converted
+    // into its slot in one pass, then the raw tile j+2 is loaded into the
+    // staging region (its own reads of it done).  In one pass the score
+    // MFMAs that follow run without waiting on the conversion's LDS traffic.
+    if constexpr (FP8) {
+      if (fp8_cv) {
+        MLA_WAIT_VMCNT(0);
+        fp8_convert_all(j + 1, Stage<s1>{});
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staging reads done before the reload
+      if (fp8_ld) fp8_load_all(j + 2);
+    }
     if (active) {
       // Scores.  The 36 MFMAs accumulate in VGPRs (inline asm: the compiler
       // would put this accumulator in AGPRs, where O already takes all 256).
@@ -1199,53 +1208,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
             if (gather) dma_step(gc, p0 + (j + 1) * kTT, gbase, Q);
           }
         }
-        if constexpr (FP8) {
-          // conversion of tile j+1, one dword of codes per MFMA (the VALU work
-          // fits beside the MFMA): unit u is read at step 8u, converted at
-          // steps 8u+2 .. 8u+5, and its staging bytes are reloaded with tile
-          // j+2 once read (scales at step 2, unit u at 8u+3, rotary at 32), so
-          // each load has about one tile of time to land.  Waits count loads
-          // in issue order: tile j+1's later loads, then tile j+2's issued ones.
-          if constexpr (k % 8 == 0 && k < 32) {
-            if (fp8_cv) {
-              constexpr int u = k / 8;
-              if (u > 0 && fp8_ld) MLA_WAIT_VMCNT(5);
-              else MLA_WAIT_VMCNT(4 - u);  // scales (first load) and unit u
-              if constexpr (u == 0) fsc = fp8_scales();
-              fq = fp8_read(Stage<u>{});
-            }
-          }
-          if constexpr (k % 8 >= 2 && k % 8 <= 5 && k < 32) {
-            if (fp8_cv) {
-              constexpr int u = k / 8, d = k % 8 - 2;
-              const u32x2 w = fp8_cvt4(fq[d], fsc[u]);
-              if constexpr (d & 1) fp8_store(slot(Stage<s1>{}), Stage<u>{}, d >> 1, u32x4{fw[0], fw[1], w[0], w[1]});
-              else fw = w;
-            }
-            if constexpr (k == 2) {
-              if (fp8_ld) fp8_load(j + 2, Stage<0>{}, __float_as_uint(fsc[0]));
-            }
-            if constexpr (k % 8 == 3) {
-              if (fp8_ld) fp8_load(j + 2, Stage<k / 8 + 1>{}, fq[0]);
-            }
-          }
-          if constexpr (k == 30) {
-            if (fp8_cv) {
-              if (fp8_ld) MLA_WAIT_VMCNT(5);
-              else MLA_WAIT_VMCNT(0);
-              fq = fp8_rope_read();
-            }
-          }
-          if constexpr (k == 31) {
-            if (fp8_cv) {
-              fp8_rope_write(slot(Stage<s1>{}), fq);
-              publish_mask(p0 + (j + 1) * kTT, s1);
-            }
-          }
-          if constexpr (k == 32) {
-            if (fp8_ld) fp8_load(j + 2, Stage<5>{}, fq[0]);
-          }
-        }
         if constexpr (k == 35) asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s));
       };
       auto group = [&](auto Q) MLA_INLINE {
@@ -1267,13 +1229,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
       full_all(ft);
     } else if (gather) {
       dma_all(gc, p0 + (j + 1) * kTT, gbase);
-    } else if (FP8) {
-      if (fp8_cv) {
-        MLA_WAIT_VMCNT(0);
-        fp8_convert_all(j + 1, Stage<s1>{});
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      if (fp8_ld) fp8_load_all(j + 2);
     }
     const uint32_t mask = sMask[st];
     // one code path for every wave inside the loop (branches around the
