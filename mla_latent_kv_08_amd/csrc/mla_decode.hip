@@ -830,12 +830,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     fo_st0 = (uint32_t)tile_off(x, 16 * wave + 2 * c) | ((uint32_t)tile_off(x, 16 * wave + 2 * c + 1) << 16);
     fo_st1 = (uint32_t)tile_off(8 + x, 16 * wave + 2 * c) | ((uint32_t)tile_off(8 + x, 16 * wave + 2 * c + 1) << 16);
   }
-  // Load n of a raw tile (issue order, which the conversion's waits count
-  // on): 0 scales, 1..4 code units 0..3, 5 rotary rows.  `dep`: a value read
-  // from the bytes this load replaces (orders the load after that read).
+  // Load n of a raw tile: 0 scales, 1..4 code units 0..3, 5 rotary rows (the
+  // staging bytes they replace have been read: the caller waits for that).
   // A dense tile of 32 selected rows takes the fixed offsets above from its
   // first row (scalar base); any other tile computes each lane's row.
-  auto fp8_load = [&](int j, auto N, uint32_t dep = 0u) MLA_INLINE {
+  auto fp8_load = [&](int j, auto N) MLA_INLINE {
+    constexpr uint32_t dep = 0u;  // no read to order after
     constexpr int n = decltype(N)::value;
     const int pt = p0 + j * kTT;
     const bool full = !TOPK && pt + kTT <= p1;
@@ -1142,10 +1142,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     if (!FP8) MLA_WAIT_VMCNT(0);
     MLA_LDS_BARRIER();
     // tile j+1: a full dense tile is loaded by the fast path, its nine loads
-    // per thread spread over the score MFMAs; any other tile in one burst here.
-    // FP8: this wave's part of tile j+1 (staged during tile j-1) is converted
-    // into its slot during the score MFMAs, then the raw tile j+2 is loaded
-    // into the staging region (its own reads of it done).
+    // per thread spread over the score MFMAs; any other tile in one burst here
+    // (the FP8 cache is staged and converted below).
     const bool fast = !FP8 && !TOPK && j + 1 < ntiles && p0 + (j + 2) * kTT <= p1;
     // top-k: the gathered tile j+1 is loaded one load per group of score
     // MFMAs too (each load looks its row up in the staged indices)
