@@ -82,27 +82,31 @@ def sources_sha():
     return h.hexdigest()[:16]
 
 
-def counter_traffic(workload, kernel_symbol):
-    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary,
-    or None when there is none for this kernel or the sources changed since."""
+def counter_traffic(workload, kernel_symbol, check_sources=True):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary
+    (first row of the workload whose symbol starts with `kernel_symbol`), or None
+    when there is none for this kernel or the sources changed since."""
     import re
     path = os.path.join(ROOT, "profiles", "hbm_traffic_counters.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"Sources at sha256 \(csrc/\*\.hip, \*\.hpp\) `([0-9a-f]+)`", text)
-    if not m or m.group(1) != sources_sha():
+    if check_sources and (not m or m.group(1) != sources_sha()):
         return None
     for line in text.splitlines():
         cells = [c.strip().strip("`") for c in line.strip().strip("|").split("|")]
-        if len(cells) == 6 and cells[0] == workload and cells[1] == kernel_symbol:
+        if len(cells) == 6 and cells[0] == workload and cells[1].startswith(kernel_symbol):
             return int(float(cells[5]))
     return None
 
 
 def kernel_symbol(name, w):
+    """The kernel's symbol as the profiles name it, or, for the attention kernel,
+    the prefix up to its last template argument (heads per wave, which the work
+    planner picks; a workload launches one instance)."""
     if name == "attention":
-        return "mla::attn_kernel<%s, %s>" % ("true" if w.fp8 else "false", "true" if w.topk else "false")
+        return "mla::attn_kernel<%s, %s, " % ("true" if w.fp8 else "false", "true" if w.topk else "false")
     if name == "cache_write":
         return "mla::cache_write_fp8_kernel" if w.fp8 else "mla::cache_write_bf16_kernel"
     if name == "absorb":  # template argument: 0 no row store, 1 bf16 rows, 2 FP8 rows
