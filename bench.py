@@ -101,6 +101,25 @@ def counter_traffic(workload, kernel_symbol, check_sources=True):
     return None
 
 
+def stream_probe(torch, nbytes=1 << 30, reps=10):
+    """Attainable HBM bandwidth measured in this run: a plain device copy of
+    `nbytes` (beyond any cache) timed with events over `reps` copies; read +
+    write bytes per second, in GB/s.  (torch's reductions read far below the
+    copy's rate on this GPU, so the copy is the reference.)"""
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    seconds = start.elapsed_time(end) * 1e-3 / reps
+    del src, dst
+    return 2 * nbytes / seconds / 1e9
+
+
 def kernel_symbol(name, w):
     """The kernel's symbol as the profiles name it, or, for the attention kernel,
     the prefix up to its last template argument (heads per wave, which the work
@@ -235,6 +254,8 @@ def main():
                          "the rows up to its own)")
     ap.add_argument("--unfused", action="store_true",
                     help="mla_cache_write then mla_decode instead of mla_decode_step")
+    ap.add_argument("--no-stream-probe", action="store_true",
+                    help="skip the device-copy measurement of attainable HBM bandwidth")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 5 plain device copies of BYTES bytes (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -346,6 +367,9 @@ def main():
     roof["traffic"] = counter_traffic(w.name, kernel_symbol(dom, w))
     roof["kernel"] = dom
     roof["avg_us"] = avg_us[dom]
+    stream_gbps = None if args.no_stream_probe else stream_probe(torch)
+    if stream_gbps and roof["bound"] == "hbm":
+        roof["frac_of_measured_stream"] = roof["achieved"] / stream_gbps
 
     tokens_per_s = B * S * args.steps / elapsed
     step_s = ms_per_step * 1e-3
@@ -376,6 +400,9 @@ def main():
         "step_hbm_gbps": total_bytes / step_s / 1e9,
         "step_hbm_frac": total_bytes / step_s / 1e9 / PEAK_HBM_GBS,
         "step_mfma_frac": total_flops / step_s / 1e12 / PEAK_BF16_TFLOPS,
+        "hbm_stream_gbps": stream_gbps,
+        "hbm_stream_probe": "1 GiB device copy, read + write bytes per second",
+        "step_hbm_frac_of_measured_stream": (total_bytes / step_s / 1e9 / stream_gbps) if stream_gbps else None,
         "kernel_avg_us": avg_us,
         "kernel_timing": "dispatch-stamped HIP events, eager pass of the same K steps",
         "roofline": roof,
