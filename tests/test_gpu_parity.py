@@ -245,6 +245,20 @@ def test_workload_full_sampled(m, name):
     run_case(m, w, x, pairs=sample_pairs(w, 64, w.seed), label=name)
 
 
+def test_long_sequences_past_2gib_offsets(m):
+    """Maximum-size offsets: two sequences of 2^20 + 64 rows (2 GiB of bf16
+    latent).  The second is full, so its last rows sit past byte offset 2^31 of
+    the cache; the first ends 7 rows short of the buffer, with NaN in the rows
+    it must not read.  Sampled (sequence, head) outputs against the oracle."""
+    T = (1 << 20) + 64
+    w = synth.Workload("long_b2_h128_t1048640", 2, 128, T, seed=77)
+    x = synth.make_inputs(w)
+    x["cache_lens"] = torch.tensor([T - 7, T], dtype=torch.int32)
+    x["kv"][0, T - 7:] = float("nan")
+    x["pe"][0, T - 7:] = float("nan")
+    run_case(m, w, x, pairs=sample_pairs(w, 6, w.seed), label=w.name)
+
+
 # ---------------------------------------------------------------- fused decode step
 
 def _upload_caches(m, w, x):
