@@ -440,9 +440,9 @@ __global__ __launch_bounds__(256, 3) void absorb_kernel(const uint16_t* __restri
 // One tile in flight per workgroup keeps the loads from ever waiting for
 // queue space (a second queued tile makes the issuing wave stall until the
 // first lands).  FP8 cache: each wave stages its part of tile j+2 (codes,
-// scales, rotary rows) in its own LDS region by direct loads, and converts
-// its part of tile j+1 to bf16(float(code) * scale) in one pass before the
-// score chain of tile j.
+// scales, rotary rows) in its own LDS region by direct loads (a dense tile's
+// spread over the score chain), and converts its part of tile j+1 to
+// bf16(float(code) * scale) in one pass before the score chain of tile j.
 //
 // LDS swizzle: logical 16-byte chunk ch of row t sits at chunk ch ^ F(t),
 // F(t) = 4((t>>1)&1) + ((t>>2)&3), which only permutes chunks inside their
@@ -833,41 +833,50 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   // Load n of a raw tile: 0 scales, 1..4 code units 0..3, 5 rotary rows (the
   // staging bytes they replace have been read: the caller waits for that).
   // A dense tile of 32 selected rows takes the fixed offsets above from its
-  // first row (scalar base); any other tile computes each lane's row.
+  // first row (scalar base): this form is also issued inside the score chain,
+  // which has no registers to spare for the general form's per-lane rows.
+  auto fp8_load_full = [&](int j, auto N) MLA_INLINE {
+    constexpr uint32_t dep = 0u;
+    constexpr int n = decltype(N)::value;
+    const size_t r0 = seq_row0 + p0 + j * kTT;
+    uint32_t base = lds_addr(fregion);
+    asm volatile("" : "+s"(base));
+    if constexpr (n >= 1 && n <= 4) {
+      constexpr int u = n - 1;
+      lds_dma16_s<1024 * u>(uniform64((const uint8_t*)a.kv + r0 * kC + 4096 * u), fresh(fo_a) & 0xFFFFu, base, dep);
+    } else if constexpr (n == 0) {
+      if (lane < 32) lds_dma4_s<kFp8WaveCodes>(uniform64(a.kv_scale + r0 * 4), fresh(fo_b) & 0xFFFFu, base, dep);
+    } else {
+      lds_dma16_s<kFp8WaveCodes + kFp8WaveScales>(uniform64(a.pe + r0 * kR), fresh(fo_b) >> 16, base, dep);
+    }
+  };
+  // Any tile (a dense one goes to the form above; any other computes each
+  // lane's row).
   auto fp8_load = [&](int j, auto N) MLA_INLINE {
     constexpr uint32_t dep = 0u;  // no read to order after
     constexpr int n = decltype(N)::value;
     const int pt = p0 + j * kTT;
-    const bool full = !TOPK && pt + kTT <= p1;
-    uint32_t base = lds_addr(fregion);
-    asm volatile("" : "+s"(base));
-    if (full) {
-      const size_t r0 = seq_row0 + pt;
-      if constexpr (n >= 1 && n <= 4) {
-        constexpr int u = n - 1;
-        lds_dma16_s<1024 * u>(uniform64((const uint8_t*)a.kv + r0 * kC + 4096 * u), fresh(fo_a) & 0xFFFFu, base, dep);
-      } else if constexpr (n == 0) {
-        if (lane < 32) lds_dma4_s<kFp8WaveCodes>(uniform64(a.kv_scale + r0 * 4), fresh(fo_b) & 0xFFFFu, base, dep);
-      } else {
-        lds_dma16_s<kFp8WaveCodes + kFp8WaveScales>(uniform64(a.pe + r0 * kR), fresh(fo_b) >> 16, base, dep);
-      }
+    if (!TOPK && pt + kTT <= p1) {
+      fp8_load_full(j, N);
       return;
     }
+    uint32_t base = lds_addr(fregion);
+    asm volatile("" : "+s"(base));
     const int ln = fresh_lane();
     if constexpr (n >= 1 && n <= 4) {
       constexpr int u = n - 1;
       const int r = 8 * u + (ln >> 3);
-      const size_t row = seq_row0 + (full ? pt + r : tile_row(pt, r));
+      const size_t row = seq_row0 + tile_row(pt, r);
       lds_dma16_after<1024 * u>((const uint8_t*)a.kv + row * kC + kBlk * wave + 16 * (ln & 7), base, dep);
     } else if constexpr (n == 0) {
       if (ln < 32) {
         const int r = 8 * (ln & 3) + (ln >> 2);
-        const size_t row = seq_row0 + (full ? pt + r : tile_row(pt, r));
+        const size_t row = seq_row0 + tile_row(pt, r);
         lds_dma4_after<kFp8WaveCodes>(a.kv_scale + row * 4 + wave, base, dep);
       }
     } else {
       const int r = 8 * wave + (ln >> 3);
-      const size_t row = seq_row0 + (full ? pt + r : tile_row(pt, r));
+      const size_t row = seq_row0 + tile_row(pt, r);
       lds_dma16_after<kFp8WaveCodes + kFp8WaveScales>(a.pe + row * kR + 8 * (ln & 7), base, dep);
     }
   };
@@ -1149,6 +1158,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     // MFMAs too (each load looks its row up in the staged indices)
     const bool gather = !FP8 && TOPK && j + 1 < ntiles;
     const bool fp8_cv = FP8 && j + 1 < ntiles, fp8_ld = FP8 && j + 2 < ntiles;
+    // a full dense tile j+2 is reloaded inside the score chain, any other in one burst
+    const bool fp8_in_chain = FP8 && !TOPK && active && fp8_ld && p0 + (j + 3) * kTT <= p1;
     const FullTile ft = full_tile(j + 1, Stage<s1>{});
     if (!FP8 && j + 1 < ntiles) {
       if (fast || gather) publish_mask(p0 + (j + 1) * kTT, s1);
@@ -1167,15 +1178,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     f32x16 s = {};  // waves without score heads run the softmax on zeros
     // FP8: this wave's part of tile j+1 (staged during tile j-1) is converted
     // into its slot in one pass, then the raw tile j+2 is loaded into the
-    // staging region (its own reads of it done).  In one pass the score
-    // MFMAs that follow run without waiting on the conversion's LDS traffic.
+    // staging region (its own reads of it done): a full dense tile by six
+    // loads spread over the score chain (issued back to back they stall the
+    // wave), any other here.  In one pass the score MFMAs that follow run
+    // without waiting on the conversion's LDS traffic.
     if constexpr (FP8) {
       if (fp8_cv) {
         MLA_WAIT_VMCNT(0);
         fp8_convert_all(j + 1, Stage<s1>{});
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staging reads done before the reload
-      if (fp8_ld) fp8_load_all(j + 2);
+      if (fp8_ld && !fp8_in_chain) fp8_load_all(j + 2);
     }
     if (active) {
       // Scores.  The 36 MFMAs accumulate in VGPRs (inline asm: the compiler
@@ -1204,6 +1217,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
           if (fast) full_load(ft, Q);
           if constexpr (TOPK && !FP8) {
             if (gather) dma_step(gc, p0 + (j + 1) * kTT, gbase, Q);
+          }
+          if constexpr (FP8 && !TOPK && decltype(Q)::value < 6) {
+            if (fp8_in_chain) fp8_load_full(j + 2, Q);
           }
         }
         if constexpr (k == 35) asm volatile("s_nop 15\n\ts_nop 3" : "+v"(s));
