@@ -216,6 +216,47 @@ def test_deterministic_and_no_out_of_bounds_writes(m):
     assert (buf[:guard] == -7.0).all() and (buf[-guard:] == -7.0).all()
 
 
+# Latent and rotary rows scaled up along the sequence (x 0.5 at row 0 to x 4.5
+# at the last row), so the logits keep growing and the running maximum moves
+# by more than the lazy-rescale threshold after the first tile (once or twice
+# for every head of the bf16 cases): the rescale of non-zero accumulators
+# runs, and several waves set the shared rescale flag at once.
+# Each instance of the attention kernel runs ten times on the same inputs;
+# every output must equal the first bit for bit, and the first the oracle.
+@pytest.mark.parametrize("B,H,T,topk,fp8", [(2, 128, 3000, 0, False),    # four head blocks
+                                            (1, 128, 4096, 0, False),    # one block, heads split four ways
+                                            (4, 128, 8192, 1024, False), # top-k, two blocks
+                                            (2, 128, 3000, 0, True)])    # FP8 cache
+def test_rescale_path_repeatable(m, B, H, T, topk, fp8):
+    w = synth.Workload(f"ramp_b{B}_h{H}_t{T}", B, H, T, fp8=fp8, topk=topk, seed=31 + B)
+    x = synth.make_inputs(w)
+    ramp = (0.5 + 4.0 * torch.arange(T, dtype=torch.float32) / T).reshape(1, T, 1)
+    x["kv"] = (x["kv"].float() * ramp).to(torch.bfloat16)
+    x["pe"] = (x["pe"].float() * ramp).to(torch.bfloat16)
+    label = f"{w.name} topk={topk} fp8={fp8}"
+    print(f"[{label}] GPU decode x10", flush=True)
+    kv, sc, pe = gpu_caches(m, w, x)
+    args = [to_dev(x["q_nope"]), to_dev(x["q_pe"]), to_dev(x["wkv_b"]), kv, pe, to_dev(x["cache_lens"])]
+    kw = dict(kv_scale=sc, topk_idx=to_dev(x["topk_idx"]))
+    first = m.decode(*args, **kw)
+    torch.cuda.synchronize()
+    for rep in range(9):
+        again = m.decode(*args, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(first.view(torch.int16), again.view(torch.int16)), (label, rep)
+    okv, osc, ope = oracle_caches(w, x)
+    ref = oracle.decode(x["q_nope"], x["q_pe"], x["wkv_b"], okv, ope, x["cache_lens"],
+                        synth.SOFTMAX_SCALE, kv_scale=osc, topk_idx=x["topk_idx"])
+    # The output is a convex combination of latent rows scaled by up to 4.5,
+    # then up-projected: absolute rounding errors scale with the rows, so the
+    # bf16 max |err| bar is scaled by the ramp's maximum; relative L2 is not.
+    rel, mx = errors(first, ref.reshape(B, 1, H, 128))
+    print(f"[{label}] relL2={rel:.3e} max|err|={mx:.3e}", flush=True)
+    assert rel <= (REL_FP8 if fp8 else REL_BF16), (label, rel)
+    if not fp8:
+        assert mx <= ABS_MAX * 4.5, (label, mx)
+
+
 # ---------------------------------------------------------------- the five workloads, full size
 
 def sample_pairs(w, n, seed):
