@@ -242,8 +242,8 @@ def cpu_baseline(w, x, seconds, oracle, synth, np, torch):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="dense_b1_h128_t4096")
     ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed the MALL")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
