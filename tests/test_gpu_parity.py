@@ -140,6 +140,21 @@ def test_topk_small(m):
     run_case(m, w, x, label="topk300")
 
 
+@pytest.mark.parametrize("H", [128, 48])
+def test_fp8_topk_small(m, H):
+    """FP8 cache with a top-k selection: the staging loads take each lane's
+    row from the staged indices (H = 48 leaves waves without score heads)."""
+    w = synth.Workload("fp8topk", 3, H, 2000, fp8=True, topk=300, outlier_frac=0.01, outlier_mult=20.0,
+                       seed=9 + H)
+    x = synth.make_inputs(w)
+    idx = x["topk_idx"].clone()
+    idx[0, 0, :7] = -1          # padding
+    idx[1, 0, -3:] = 5000       # out of range
+    x["topk_idx"] = idx
+    x["cache_lens"] = torch.tensor([2000, 1500, 2000], dtype=torch.int32)  # b1: entries >= 1500 skipped
+    run_case(m, w, x, label=f"fp8 topk300 H{H}")
+
+
 def test_topk_all_positions_equals_dense(m):
     w = synth.Workload("dense", 2, 128, 160, seed=7)
     x = synth.make_inputs(w)
@@ -311,8 +326,8 @@ def _upload_caches(m, w, x):
     return torch.from_numpy(codes), torch.from_numpy(scales), torch.from_numpy(pe.view(np.int16)).view(torch.bfloat16)
 
 
-@pytest.mark.parametrize("fp8,topk,B", [(False, 0, 5), (True, 0, 5), (False, 96, 3), (True, 0, 2100),
-                                        (False, 0, 2100)])
+@pytest.mark.parametrize("fp8,topk,B", [(False, 0, 5), (True, 0, 5), (False, 96, 3), (True, 96, 3),
+                                        (True, 0, 2100), (False, 0, 2100)])
 def test_decode_step_writes_then_attends(m, fp8, topk, B):
     T = 70 if B > 100 else 300
     w = synth.Workload("step", B, 16 if B > 100 else 128, T, fp8=fp8, topk=topk, ragged=(0, T), seed=12 + B)
@@ -386,7 +401,8 @@ def host_caches(x, T, fp8):
 
 
 @pytest.mark.parametrize("B,s,H,T,fp8,topk", [(3, 3, 32, 150, False, 0), (2, 2, 128, 300, False, 0),
-                                              (3, 4, 16, 97, True, 0), (2, 2, 128, 400, False, 64)])
+                                              (3, 4, 16, 97, True, 0), (2, 2, 128, 400, False, 64),
+                                              (2, 2, 128, 400, True, 64)])
 def test_multitoken_decode(m, B, s, H, T, fp8, topk):
     x = multitoken_case(B, s, H, T, fp8, topk, seed=31 + s + T)
     kv, sc, pe = host_caches(x, T, fp8)
