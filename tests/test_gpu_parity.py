@@ -155,6 +155,20 @@ def test_fp8_topk_small(m, H):
     run_case(m, w, x, label=f"fp8 topk300 H{H}")
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+def test_topk_unsplit_workgroups(m, fp8):
+    """Top-k with 144 plan workgroups (9 sequences x 2048 selected rows, 4 tiles
+    each): no head split, every workgroup scores all four head blocks; the
+    2048-of-65536 workload (8 sequences, 128 workgroups) splits them in two."""
+    w = synth.Workload("topk_unsplit", 9, 128, 3000, fp8=fp8, topk=2048, seed=21 + int(fp8))
+    x = synth.make_inputs(w)
+    idx = x["topk_idx"].clone()
+    idx[0, 0, :11] = -1         # padding
+    idx[4, 0, -2:] = 7000       # out of range
+    x["topk_idx"] = idx
+    run_case(m, w, x, pairs=sample_pairs(w, 48, w.seed), label=f"topk unsplit fp8={fp8}")
+
+
 def test_topk_all_positions_equals_dense(m):
     w = synth.Workload("dense", 2, 128, 160, seed=7)
     x = synth.make_inputs(w)
