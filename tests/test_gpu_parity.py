@@ -286,6 +286,32 @@ def test_rescale_path_repeatable(m, B, H, T, topk, fp8):
         assert mx <= ABS_MAX * 4.5, (label, mx)
 
 
+def test_concurrent_streams_match_sequential(m):
+    """The library keeps no device state between calls: two decodes with their
+    own workspaces, issued alternately on two streams (default priority) so
+    that they may overlap, give bit for bit the outputs of the same calls
+    made one after another."""
+    cases = []
+    for w in [synth.Workload("concA", 4, 128, 3000, ragged=(100, 3000), seed=71),
+              synth.Workload("concB", 3, 128, 2000, fp8=True, topk=300, seed=72)]:
+        x = synth.make_inputs(w)
+        kv, sc, pe = gpu_caches(m, w, x)
+        args = [to_dev(x["q_nope"]), to_dev(x["q_pe"]), to_dev(x["wkv_b"]), kv, pe, to_dev(x["cache_lens"])]
+        kw = dict(kv_scale=sc, topk_idx=to_dev(x["topk_idx"]))
+        ref = m.decode(*args, **kw)
+        p = m.make_params(w.batch, w.heads, w.max_seq_len, 1 if w.fp8 else 0, topk=w.topk)
+        ws = torch.empty(m.decode_workspace_size(p), dtype=torch.uint8, device=DEV)
+        cases.append((args, kw, ref, torch.empty_like(ref), ws))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(5):
+        for (args, kw, _, out, ws), st in zip(cases, streams):
+            m.decode(*args, **kw, out=out, workspace=ws, stream=st)
+        torch.cuda.synchronize()
+        for args, kw, ref, out, ws in cases:
+            assert torch.equal(ref.view(torch.int16), out.view(torch.int16)), rep
+
+
 # ---------------------------------------------------------------- the five workloads, full size
 
 def sample_pairs(w, n, seed):
