@@ -392,6 +392,75 @@ def test_fp8_dequant_error_bound():
     assert (np.abs(deq - lat) <= bound).all()
 
 
+def _codes_by_division_then_cast(kv_bf16):
+    """Block codes of the cache-write excerpt computed independently of the
+    oracle: the block maximum of the bf16 values widened to fp32, the scale
+    amax / 448 and every quotient x / scale as IEEE fp32 divisions (numpy),
+    then torch's own float8_e4m3fn cast (round to nearest even), clamped to
+    +-448 first because the cast does not saturate; code 0 where the scale
+    is 0."""
+    x = kv_bf16.to(torch.float32).numpy().reshape(-1, 128)
+    amax = np.abs(x).max(axis=1)
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = (x / scale[:, None]).astype(np.float32)
+    q = np.where(scale[:, None] > 0, q, np.float32(0.0))
+    q = np.clip(q, np.float32(-448.0), np.float32(448.0))
+    codes = torch.from_numpy(q).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    codes = np.where(scale[:, None] > 0, codes, np.uint8(0))
+    return codes.reshape(kv_bf16.shape), scale.reshape(kv_bf16.shape[:-1] + (4,))
+
+
+def _fp8_pin_blocks():
+    """Latent rows [1, T, 512] whose 128-element blocks exercise the quantiser:
+    c3-style draws (N(0, 1), 1 % of entries x20), scales that are powers of
+    two with every element on an E4M3 midpoint (ties after the division),
+    all-zero blocks, blocks of tiny or subnormal bf16 values, a negative block
+    maximum, and signed zeros."""
+    g = torch.Generator().manual_seed(31)
+    rows = []
+    base = torch.randn(3000, 512, generator=g)
+    out = torch.rand(3000, 512, generator=g) < 0.01
+    rows.append(torch.where(out, base * 20.0, base))
+    pos = np.array([oracle.e4m3fn_value(c) for c in range(0x7F)], np.float64)
+    mids = (pos[1:] + pos[:-1]) / 2                       # 126 midpoints, exact in bf16
+    for k in (-20, -3, 0, 5, 30):
+        blk = np.zeros(128)
+        blk[0] = 448.0
+        blk[1:127] = mids
+        blk[127] = -mids[-1]
+        blk = blk * 2.0 ** k                              # scale = 2^k exactly
+        sgn = np.where(np.arange(128) % 3 == 1, -1.0, 1.0)
+        sgn[0] = 1.0
+        rows.append(torch.from_numpy(np.tile(blk * sgn, 4)).float().reshape(1, 512))
+    special = torch.zeros(6, 512)
+    special[0, 128:256] = torch.randn(128, generator=g) * 1e-38         # tiny amax
+    special[1, :128] = 2.0 ** -133 * torch.arange(128).float()           # bf16 subnormals
+    special[2, 256:384] = -torch.rand(128, generator=g) - 1.0            # negative maximum
+    special[2, 300] = -7.0
+    special[3, :] = torch.randn(512, generator=g) * 1e-3
+    special[3, 5] = -0.0
+    special[3, 384:] = -0.0                                             # block of -0: scale 0
+    special[4, :128] = torch.randn(128, generator=g)
+    special[4, 7] = 3.0e38                                              # huge maximum
+    special[5, 128:256] = torch.randn(128, generator=g) * 2.0 ** 100
+    rows.append(special)
+    return torch.cat(rows).to(torch.bfloat16).reshape(1, -1, 512)
+
+
+def test_fp8_block_codes_equal_division_then_cast():
+    kv = _fp8_pin_blocks()
+    T = kv.shape[1]
+    pe = torch.zeros(1, T, 64, dtype=torch.bfloat16)
+    codes, scales, _ = oracle.cache_write(kv, pe, torch.zeros(1, dtype=torch.int32), T, True)
+    ref_codes, ref_scales = _codes_by_division_then_cast(kv)
+    assert np.array_equal(scales.view(np.uint32), ref_scales.view(np.uint32))
+    bad = np.argwhere(codes != ref_codes)
+    assert bad.size == 0, f"{len(bad)} codes differ, first at {bad[:3].tolist()}"
+    # the cases are really there: ties went to even codes, zero blocks gave scale 0
+    assert (scales == 0).sum() >= 8 and (codes == 0x80).any()
+
+
 def test_fp8_zero_block_gives_zero_scale_and_codes():
     kv = torch.zeros(1, 1, 512, dtype=torch.bfloat16)
     kv[0, 0, 128:256] = torch.randn(128).to(torch.bfloat16)
