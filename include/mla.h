@@ -21,7 +21,12 @@
  *    record into a HIP graph.
  *  - Host-side argument checks run before any HIP call; on failure nothing is
  *    enqueued and the status says why (mla_last_error() gives a detail text
- *    for the calling thread).  A launch failure returns MLA_ERR_HIP.
+ *    for the calling thread).  A launch failure returns MLA_ERR_HIP; the
+ *    status is that launch's own, not an error an earlier HIP call left on
+ *    the thread.  A call that launches several kernels (mla_decode,
+ *    mla_decode_step) and fails at its k-th launch leaves kernels 0..k-1
+ *    enqueued on the stream: the output is then undefined, and the caller
+ *    should treat the stream as failed.
  *  - Calls from several host threads are safe; calls that write the same
  *    buffers must be ordered by the caller (same stream or events).
  */

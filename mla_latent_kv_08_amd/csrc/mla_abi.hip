@@ -48,6 +48,19 @@ mla_status check_params(const mla_params* p) {
   return MLA_OK;
 }
 
+// Checks of the decode shape, shared by mla_decode_workspace_size and the
+// decode entry points (the plan is only formed for shapes that pass them).
+mla_status check_decode_shape(const mla_params* p) {
+  if (p->seqlen_q < 1) return fail(MLA_ERR_INVALID_ARG, "seqlen_q = %d < 1", p->seqlen_q);
+  if (p->num_heads < 1 || p->num_heads > MLA_MAX_HEADS)
+    return fail(MLA_ERR_INVALID_ARG, "num_heads = %d outside 1..128", p->num_heads);
+  if (p->topk < 0 || p->topk > p->max_seq_len)
+    return fail(MLA_ERR_INVALID_ARG, "topk = %d outside 0..max_seq_len", p->topk);
+  if ((long long)p->batch * p->seqlen_q > 65535)
+    return fail(MLA_ERR_UNSUPPORTED, "batch * seqlen_q > 65535 query tokens");
+  return MLA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -95,11 +108,8 @@ mla_status mla_decode_workspace_size(const mla_params* p, size_t* bytes) {
   mla_status st = check_params(p);
   if (st != MLA_OK) return st;
   if (!bytes) return fail(MLA_ERR_INVALID_ARG, "bytes is NULL");
-  if (p->num_heads < 1 || p->num_heads > MLA_MAX_HEADS)
-    return fail(MLA_ERR_INVALID_ARG, "num_heads = %d outside 1..128", p->num_heads);
-  if (p->topk < 0 || p->topk > p->max_seq_len)
-    return fail(MLA_ERR_INVALID_ARG, "topk = %d outside 0..max_seq_len", p->topk);
-  if (p->seqlen_q < 1) return fail(MLA_ERR_INVALID_ARG, "seqlen_q = %d < 1", p->seqlen_q);
+  st = check_decode_shape(p);
+  if (st != MLA_OK) return st;
   const mla::DecodePlan plan = mla::make_decode_plan(*p);
   if (plan.max_groups > 0x7FFFFFFFLL || plan.max_groups * plan.heads_padded > (1LL << 40))
     return fail(MLA_ERR_UNSUPPORTED, "too many attention workgroups for this batch and top-k");
@@ -119,15 +129,10 @@ mla_status check_decode(const mla_params* p, const void* q_nope, const void* q_p
                         void* out, void* workspace, size_t workspace_bytes, mla::DecodePlan* plan) {
   mla_status st = check_params(p);
   if (st != MLA_OK) return st;
-  if (p->seqlen_q < 1) return fail(MLA_ERR_INVALID_ARG, "seqlen_q = %d < 1", p->seqlen_q);
-  if (p->num_heads < 1 || p->num_heads > MLA_MAX_HEADS)
-    return fail(MLA_ERR_INVALID_ARG, "num_heads = %d outside 1..128", p->num_heads);
-  if (p->topk < 0 || p->topk > p->max_seq_len)
-    return fail(MLA_ERR_INVALID_ARG, "topk = %d outside 0..max_seq_len", p->topk);
+  st = check_decode_shape(p);
+  if (st != MLA_OK) return st;
   if (!(p->softmax_scale > 0.0f) || !isfinite(p->softmax_scale))
     return fail(MLA_ERR_INVALID_ARG, "softmax_scale must be finite and > 0");
-  if ((long long)p->batch * p->seqlen_q > 65535)
-    return fail(MLA_ERR_UNSUPPORTED, "batch * seqlen_q > 65535 query tokens");
   if (p->batch == 0) return MLA_OK;
   const bool fp8 = p->kv_dtype == MLA_KV_FP8_E4M3_B128;
   if (!q_nope || !q_pe || !wkv_b || !kv_cache || !pe_cache || !cache_lens || !out)

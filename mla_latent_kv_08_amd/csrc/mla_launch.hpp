@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+
 #include "mla.h"
 
 namespace mla {
@@ -36,15 +38,26 @@ struct CacheWriteArgs {
 hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWriteArgs* write,
                          hipStream_t stream);
 
-// Launch `kernel` on `stream`.  With `ev` non-null the start and end of the
-// dispatch are stamped into ev[0] and ev[1] by the dispatch itself (no extra
-// queue packets, so the elapsed time is the kernel's own duration).
+// Launch `kernel` on `stream` and return the launch's own status (not the
+// thread's last error, which an earlier unrelated HIP call may have left).
+// With `ev` non-null the start and end of the dispatch are stamped into ev[0]
+// and ev[1] by the dispatch itself (no extra queue packets, so the elapsed
+// time is the kernel's own duration).
 template <typename... KArgs, typename... Args>
 hipError_t launch_kernel_lds(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t lds_bytes,
                              hipStream_t stream, hipEvent_t const* ev, Args... args) {
-  if (ev) hipExtLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, ev[0], ev[1], 0, args...);
-  else hipLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, args...);
-  return hipGetLastError();
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count of the kernel");
+  // each argument converted to the kernel's parameter type, then passed by address
+  std::tuple<KArgs...> vals{static_cast<KArgs>(args)...};
+  return std::apply(
+      [&](auto&... v) -> hipError_t {
+        void* ptrs[] = {(void*)&v...};
+        if (ev)
+          return hipExtLaunchKernel((const void*)kernel, grid, block, ptrs, lds_bytes, stream, ev[0],
+                                    ev[1], 0);
+        return hipLaunchKernel((const void*)kernel, grid, block, ptrs, lds_bytes, stream);
+      },
+      vals);
 }
 template <typename... KArgs, typename... Args>
 hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,

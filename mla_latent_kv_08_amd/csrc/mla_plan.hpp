@@ -45,19 +45,22 @@ inline DecodePlan make_decode_plan(const mla_params& p) {
   DecodePlan d{};
   // B: query tokens, batch x seqlen_q (each token is planned as a sequence of
   // its own over the rows it sees)
-  const int B = p.batch * (p.seqlen_q > 0 ? p.seqlen_q : 1), H = p.num_heads;
+  // (64-bit: the product is formed before the caller's limit on it is known
+  // to hold; mla_decode rejects batch x seqlen_q > 65535)
+  const long long B = (long long)p.batch * (p.seqlen_q > 0 ? p.seqlen_q : 1);
+  const int H = p.num_heads;
   d.heads_padded = (H + 31) / 32 * 32;
   d.head_blocks = d.heads_padded / 32;
   const long long n_max = p.topk > 0 ? p.topk : p.max_seq_len;
   d.max_tiles = (n_max + kTileRows - 1) / kTileRows;
   d.min_group_tiles = p.topk > 0 ? 4 : 2;
-  long long G = B > kTargetCUs ? B : kTargetCUs;
+  long long G = B > kTargetCUs ? B : (long long)kTargetCUs;
   if (p.topk > 0) {
-    const long long capped = (long long)B * ((d.max_tiles + kMaxTopkGroupTiles - 1) / kMaxTopkGroupTiles);
+    const long long capped = B * ((d.max_tiles + kMaxTopkGroupTiles - 1) / kMaxTopkGroupTiles);
     if (G < capped) G = capped;
   }
   // no sequence takes more than ceil(max_tiles / min_group_tiles) workgroups
-  const long long bound = (long long)B * ((d.max_tiles + d.min_group_tiles - 1) / d.min_group_tiles);
+  const long long bound = B * ((d.max_tiles + d.min_group_tiles - 1) / d.min_group_tiles);
   if (G > bound) G = bound;
   G = (G + 7) / 8 * 8;  // whole rows of the XCD placement
   d.max_groups = G;
