@@ -12,6 +12,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla.so")
 SOURCES = ["mla_abi.hip", "mla_cache_write.hip", "mla_decode.hip"]
+# the benchmark's HBM read-rate probe: a library of its own, not part of the ABI
+PROBE_LIB = os.path.join(PKG, "libhbmprobe.so")
+PROBE_SOURCE = "hbm_probe.hip"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -36,6 +39,11 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     os.replace(LIB + ".tmp", LIB)
     for o in objs:
         os.remove(o)
+    cmd = [HIPCC, *FLAGS, "-shared", os.path.join(CSRC, PROBE_SOURCE), "-o", PROBE_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(PROBE_LIB + ".tmp", PROBE_LIB)
     return LIB
 
 

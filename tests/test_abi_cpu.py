@@ -130,6 +130,20 @@ def test_workspace_size_is_host_only_and_monotone(m):
         m.decode_workspace_size(m.make_params(8, 128, 4096, seqlen_q=0))
 
 
+def test_workspace_size_applies_the_decode_limits(m):
+    # the same query-token limit as mla_decode, checked before any plan is
+    # formed: batch x seqlen_q beyond 2^31 must not wrap to a small size
+    for batch, s in ((40000, 2), (65536, 1), (1 << 20, 1 << 12), (0x7FFFFFFF, 2)):
+        n = ctypes.c_size_t(12345)
+        st = m.lib.mla_decode_workspace_size(ctypes.byref(m.make_params(batch, 16, 100, seqlen_q=s)),
+                                             ctypes.byref(n))
+        assert st == 2 and n.value == 12345, (batch, s, st)
+        assert "65535" in m.lib.mla_last_error().decode()
+    assert m.decode_workspace_size(m.make_params(65535, 16, 100)) > 0
+    with pytest.raises(m.MLAError):
+        m.decode_workspace_size(m.make_params(1, 16, 100, topk=101))
+
+
 def test_decode_step_rejects_bad_arguments(m):
     P = m.make_params
 

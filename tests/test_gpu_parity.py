@@ -2,8 +2,13 @@
 
 Bars (float outputs are compared in float64 against the oracle's fp64 result):
   bf16 latent cache:  relative L2 <= 1e-2 and max |err| <= 5e-2
-  FP8 latent cache:   relative L2 <= 3e-2 (max |err| is printed, not bounded:
-                      with 1% of latent entries x20 the outputs reach |out| ~ 5)
+  FP8 latent cache:   relative L2 <= 1e-2 and max |err| <= 5e-2 * max(1, max|ref|).
+                      Both sides read the same dequantised values
+                      bf16(code * scale), so the FP8 cache gets the bf16 bar; only
+                      the absolute bound follows the outputs' magnitude (with 1 %
+                      of latent entries x20 they reach |out| ~ 5).  The looser
+                      3e-2 relative bound stated for an FP8 cache would not see a
+                      several-fold regression of this path.
   FP8 codes and scales written by mla_cache_write: bit-exact.
 Small cases span several 32-row tiles with ragged tails and are compared in
 full; the five decode workloads at full size run in the launch configuration
@@ -18,7 +23,7 @@ from mla_latent_kv_08_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-REL_BF16, ABS_MAX, REL_FP8 = 1e-2, 5e-2, 3e-2
+REL_BF16, ABS_MAX = 1e-2, 5e-2
 DEV = "cuda:0"
 
 
@@ -39,12 +44,15 @@ def errors(out_gpu, ref):
     return float(rel), float(np.abs(g - ref).max())
 
 
+def abs_bar(ref, fp8):
+    return ABS_MAX * max(1.0, float(np.abs(ref).max())) if fp8 else ABS_MAX
+
+
 def check(out_gpu, ref, fp8=False, label=""):
     rel, mx = errors(out_gpu, ref)
-    print(f"[{label}] relL2={rel:.3e} max|err|={mx:.3e}", flush=True)
-    assert rel <= (REL_FP8 if fp8 else REL_BF16), (label, rel)
-    if not fp8:
-        assert mx <= ABS_MAX, (label, mx)
+    print(f"[{label}] relL2={rel:.3e} max|err|={mx:.3e} max|ref|={np.abs(ref).max():.3e}", flush=True)
+    assert rel <= REL_BF16, (label, rel)
+    assert mx <= abs_bar(ref, fp8), (label, mx)
 
 
 def gpu_caches(m, w, x):
@@ -281,9 +289,8 @@ def test_rescale_path_repeatable(m, B, H, T, topk, fp8):
     # bf16 max |err| bar is scaled by the ramp's maximum; relative L2 is not.
     rel, mx = errors(first, ref.reshape(B, 1, H, 128))
     print(f"[{label}] relL2={rel:.3e} max|err|={mx:.3e}", flush=True)
-    assert rel <= (REL_FP8 if fp8 else REL_BF16), (label, rel)
-    if not fp8:
-        assert mx <= ABS_MAX * 4.5, (label, mx)
+    assert rel <= REL_BF16, (label, rel)
+    assert mx <= abs_bar(ref, fp8) * 4.5, (label, mx)
 
 
 def test_concurrent_streams_match_sequential(m):
@@ -315,11 +322,15 @@ def test_concurrent_streams_match_sequential(m):
 # ---------------------------------------------------------------- the five workloads, full size
 
 def sample_pairs(w, n, seed):
+    """n (sequence, head) rows: the four corners, then one random head of
+    every sequence (so no ragged length goes unchecked), then random rows."""
     rng = np.random.default_rng(seed)
     b = rng.integers(0, w.batch, n)
     h = rng.integers(0, w.heads, n)
     b[:4] = [0, w.batch - 1, 0, w.batch - 1]
     h[:4] = [0, w.heads - 1, w.heads - 1, 0]
+    every = np.arange(w.batch)[: max(0, n - 4)]
+    b[4:4 + len(every)] = every
     return [(int(i), int(j)) for i, j in zip(b, h)]
 
 
