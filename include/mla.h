@@ -198,6 +198,32 @@ mla_status mla_decode_step(const mla_params* p, const void* kv_new, const void* 
                            const int32_t* cache_lens, const int32_t* topk_idx, void* out,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * mla_decode_noalloc -- mla_decode without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same arguments, results, checks and errors as mla_decode, minus workspace
+ * and workspace_bytes.  The workspace is a static device array of
+ * MLA_NOALLOC_SCRATCH_BYTES inside the library: each GPU the call runs on
+ * holds one copy from the first call on it until the process ends.  The call
+ * allocates nothing (no hipMalloc, no hipFree, no allocating library
+ * routine); its first call on a device looks the array's address up
+ * (hipGetSymbolAddress), preferably outside graph capture.
+ *   - A call whose mla_decode_workspace_size exceeds the scratch size is
+ *     rejected with MLA_ERR_WORKSPACE and enqueues nothing.
+ *   - Every call on one GPU shares that GPU's scratch: two calls that may
+ *     overlap on one GPU (concurrent streams, or host threads without an
+ *     ordering between them) race and give undefined outputs.  Calls on one
+ *     stream, or otherwise ordered, are safe.  The scratch keeps the last
+ *     call's contents; no call relies on them.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20) /* 64 MiB per GPU */
+mla_status mla_decode_noalloc(const mla_params* p, const void* q_nope, const void* q_pe,
+                              const void* wkv_b, const void* kv_cache, const float* kv_scale,
+                              const void* pe_cache, const int32_t* cache_lens,
+                              const int32_t* topk_idx, void* out, void* stream);
+
 /* Static text for a status code. */
 const char* mla_status_string(mla_status s);
 

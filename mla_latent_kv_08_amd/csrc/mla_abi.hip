@@ -5,9 +5,20 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "mla.h"
 #include "mla_launch.hpp"
 #include "mla_plan.hpp"
+
+// Static device scratch of mla_decode_noalloc: the workspace of one call, in
+// a file-scope device array each GPU holds from the library's first use on it
+// until the process ends.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address on each GPU comes from
+// hipGetSymbolAddress (once per device, with that device current) and only
+// that address is ever passed to a kernel.
+static __device__ __align__(256) char scratch[MLA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -156,6 +167,40 @@ mla_status check_decode(const mla_params* p, const void* q_nope, const void* q_p
   return MLA_OK;
 }
 
+constexpr size_t kScratchBytes = (size_t)MLA_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device); NULL with the status in *st on failure.
+void* scratch_on_current_device(mla_status* st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *st = fail(MLA_ERR_HIP, "HIP: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *st = fail(MLA_ERR_UNSUPPORTED, "device %d: the static scratch covers devices 0..%d", dev,
+               kMaxDevices - 1);
+    return nullptr;
+  }
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return ptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!ptr) {
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *st = fail(MLA_ERR_HIP, "HIP: hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+  }
+  return ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -189,6 +234,31 @@ mla_status mla_decode_step(const mla_params* p, const void* kv_new, const void* 
   mla::DecodeArgs d{q_nope, q_pe, wkv_b, kv_cache, kv_scale, pe_cache, cache_lens, topk_idx, out, workspace};
   mla::CacheWriteArgs c{kv_new, pe_new, nullptr, kv_cache, kv_scale, pe_cache};
   const hipError_t e = mla::launch_decode(*p, d, &c, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "HIP: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
+
+extern "C" {
+
+mla_status mla_decode_noalloc(const mla_params* p, const void* q_nope, const void* q_pe,
+                              const void* wkv_b, const void* kv_cache, const float* kv_scale,
+                              const void* pe_cache, const int32_t* cache_lens,
+                              const int32_t* topk_idx, void* out, void* stream) {
+  // validate against the scratch size first (no HIP call for a rejected call);
+  // any non-null 16-byte aligned value stands for the scratch in this check
+  mla::DecodePlan plan;
+  mla_status st = check_decode(p, q_nope, q_pe, wkv_b, kv_cache, kv_scale, pe_cache, cache_lens,
+                               topk_idx, out, (void*)(uintptr_t)256, kScratchBytes, &plan);
+  if (st == MLA_ERR_WORKSPACE)
+    return fail(MLA_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the static scratch holds %zu",
+                plan.bytes, kScratchBytes);
+  if (st != MLA_OK || p->batch == 0) return st == MLA_OK ? ok() : st;
+  void* ws = scratch_on_current_device(&st);
+  if (!ws) return st;
+  mla::DecodeArgs d{q_nope, q_pe, wkv_b, kv_cache, kv_scale, pe_cache, cache_lens, topk_idx, out, ws};
+  const hipError_t e = mla::launch_decode(*p, d, nullptr, (hipStream_t)stream);
   if (e != hipSuccess) return fail(MLA_ERR_HIP, "HIP: %s", hipGetErrorString(e));
   return ok();
 }

@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libmla.so")
 
 C_LATENT, R_ROPE, D_NOPE, D_V = 512, 64, 128, 128
 KV_BF16, KV_FP8_E4M3_B128 = 0, 1
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MLA_NOALLOC_SCRATCH_BYTES
 DEFAULT_SOFTMAX_SCALE = 1.0 / math.sqrt(D_NOPE + R_ROPE)
 
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
@@ -58,6 +59,8 @@ def _load():
     L.mla_decode.argtypes = [P] + [vp] * 10 + [ctypes.c_size_t, vp]
     L.mla_decode_step.restype = ctypes.c_int
     L.mla_decode_step.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, vp]
+    L.mla_decode_noalloc.restype = ctypes.c_int
+    L.mla_decode_noalloc.argtypes = [P] + [vp] * 10
     L.mla_status_string.restype = ctypes.c_char_p
     L.mla_status_string.argtypes = [ctypes.c_int]
     L.mla_last_error.restype = ctypes.c_char_p
@@ -168,4 +171,21 @@ def decode_step(kv_new, pe_new, q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_l
                                _ptr(q_pe), _ptr(wkv_b), _ptr(kv_cache), _ptr(kv_scale),
                                _ptr(pe_cache), _ptr(cache_lens), _ptr(topk_idx), _ptr(out),
                                _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def decode_noalloc(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, out, kv_scale=None,
+                   topk_idx=None, softmax_scale=DEFAULT_SOFTMAX_SCALE, stream=None):
+    """mla_decode_noalloc: mla_decode on the library's static device scratch
+    (no workspace argument); `out` [B,s,H,128] bf16 must be given, since this
+    path allocates nothing.  Calls that may overlap on one GPU race."""
+    _dev(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, kv_scale, topk_idx, out)
+    B, s, H = q_nope.shape[0], q_nope.shape[1], q_nope.shape[2]
+    fp8 = kv_scale is not None
+    k = 0 if topk_idx is None else topk_idx.shape[-1]
+    p = make_params(B, H, kv_cache.shape[1], KV_FP8_E4M3_B128 if fp8 else KV_BF16, topk=k,
+                    seqlen_q=s, softmax_scale=softmax_scale)
+    _check(lib.mla_decode_noalloc(ctypes.byref(p), _ptr(q_nope), _ptr(q_pe), _ptr(wkv_b),
+                                  _ptr(kv_cache), _ptr(kv_scale), _ptr(pe_cache), _ptr(cache_lens),
+                                  _ptr(topk_idx), _ptr(out), _stream(stream)))
     return out

@@ -161,3 +161,30 @@ def test_decode_step_rejects_bad_arguments(m):
     assert step(P(1, 16, 100, seqlen_q=0)) == 1
     assert step(P(1, 16, 100), ws_bytes=16) == 3
     assert step(P(0, 16, 100), kv_new=None) == 0                            # empty batch: no-op
+
+
+def test_decode_noalloc_rejects_before_any_hip_call(m):
+    P = m.make_params
+
+    def na(p, **kw):
+        a = dict(q_nope=FAKE, q_pe=FAKE, wkv_b=FAKE, kv=FAKE, scale=None, pe=FAKE, lens=FAKE,
+                 topk=None, out=FAKE)
+        a.update(kw)
+        return m.lib.mla_decode_noalloc(ctypes.byref(p), a["q_nope"], a["q_pe"], a["wkv_b"], a["kv"],
+                                        a["scale"], a["pe"], a["lens"], a["topk"], a["out"], None)
+
+    # a call whose workspace exceeds the static scratch: MLA_ERR_WORKSPACE, nothing enqueued
+    big = P(2000, 128, 4096)
+    assert m.decode_workspace_size(big) > m.NOALLOC_SCRATCH_BYTES
+    assert na(big) == 3
+    assert "static scratch holds %d" % m.NOALLOC_SCRATCH_BYTES in m.lib.mla_last_error().decode()
+    # the benchmark's workloads fit it
+    for B, T, k, s in ((32, 16384, 0, 1), (16, 32768, 0, 1), (8, 65536, 2048, 1), (1, 4096, 0, 1),
+                       (32, 16384, 0, 2)):
+        assert m.decode_workspace_size(P(B, 128, T, topk=k, seqlen_q=s)) <= m.NOALLOC_SCRATCH_BYTES
+    # the same argument checks as mla_decode
+    assert na(P(1, 16, 100), q_pe=None) == 1
+    assert na(P(1, 16, 100, kv_dtype=1)) == 1
+    assert na(P(1, 129, 100)) == 1
+    assert na(P(40000, 16, 100, seqlen_q=2)) == 2
+    assert na(P(0, 16, 100)) == 0
