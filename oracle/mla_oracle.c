@@ -17,6 +17,10 @@
  *  - "DeepSeek MLA Architecture: ... cuts KV cache by 93%", section 3
  *    (score = content term + rotary term, k_R shared by all heads) and
  *    section 4 (absorbed query; values aggregated in latent space, then W_UV).
+ *  - The same article, sections 4-5: the output projection W_O applied to
+ *    the heads' up-projected outputs concatenated (feature 128 h + d), and
+ *    its offline fusion with the value half, W_OV = W_O W_UV per head,
+ *    applied to the latent output (feature 512 h + c).
  *  - OCP 8-bit floating point specification, E4M3 ("FN": no infinities,
  *    S.1111.111 is NaN, largest finite 448).
  *
@@ -204,8 +208,10 @@ static double latent_at(int fp8, const void* kv_cache, const float* kv_scale, si
 
 /* One (query token q = b * s + i, head h) output row out[128]; optionally
  * the softmax probabilities over positions 0..max_seq_len-1 (0 where not
- * selected). */
-static void decode_one(const oracle_decode_args* a, int q, int h, double* out, double* probs) {
+ * selected) and the latent output o[512] of step 4 (before the
+ * up-projection).  out may be NULL when only the latent output is wanted. */
+static void decode_one(const oracle_decode_args* a, int q, int h, double* out, double* probs,
+                       double* latent) {
   const int T = a->max_seq_len;
   const int b = q / a->s, i_tok = q % a->s;
   int end = a->cache_lens[b];
@@ -276,8 +282,10 @@ static void decode_one(const oracle_decode_args* a, int q, int h, double* out, d
     for (int c = 0; c < ORC_C; ++c) o[c] += score[t] * latent_at(a->fp8, a->kv_cache, a->kv_scale, row, c);
   }
 
+  if (latent) memcpy(latent, o, sizeof o);
+
   /* Step 5, up-project: out[d] = sum_c o[c] * wkv_b[h, 128 + d, c]. */
-  for (int d = 0; d < ORC_DV; ++d) {
+  for (int d = 0; out && d < ORC_DV; ++d) {
     double acc = 0.0;
     for (int c = 0; c < ORC_C; ++c) {
       double w = oracle_bf16_value(a->wkv_b[((size_t)h * (ORC_DN + ORC_DV) + ORC_DN + d) * ORC_C + c]);
@@ -299,7 +307,50 @@ int oracle_decode(const oracle_decode_args* a, int n_pairs, const int32_t* pairs
   for (int i = 0; i < n; ++i) {
     int q = pairs ? pairs[2 * i] : i / a->H;
     int h = pairs ? pairs[2 * i + 1] : i % a->H;
-    decode_one(a, q, h, out + (size_t)i * ORC_DV, probs ? probs + (size_t)i * a->max_seq_len : NULL);
+    decode_one(a, q, h, out + (size_t)i * ORC_DV, probs ? probs + (size_t)i * a->max_seq_len : NULL,
+               NULL);
+  }
+  return 0;
+}
+
+/* The latent attention output of steps 1-4 for the same (q, h) pairs:
+ * olat: double [n][C], o[c] = sum_t p[t] c_KV[t, c] (MLA article, section 4:
+ * the weights multiply the cached 512-wide latents directly; the value
+ * up-projection comes after). */
+int oracle_decode_latent(const oracle_decode_args* a, int n_pairs, const int32_t* pairs,
+                         double* olat) {
+  if (!a || a->B < 0 || a->H <= 0 || a->max_seq_len <= 0 || a->topk < 0 || a->s < 1) return 1;
+  if (a->topk > 0 && !a->topk_idx) return 1;
+  if (a->fp8 && !a->kv_scale) return 1;
+  if (!olat) return 1;
+  int n = pairs ? n_pairs : a->B * a->s * a->H;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int i = 0; i < n; ++i) {
+    int q = pairs ? pairs[2 * i] : i / a->H;
+    int h = pairs ? pairs[2 * i + 1] : i % a->H;
+    decode_one(a, q, h, NULL, NULL, olat + (size_t)i * ORC_C);
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* Output projection (MLA article, section 5: W_O after the value      */
+/* up-projection; section 4: W_OV = W_O W_UV fused offline)            */
+/* ------------------------------------------------------------------ */
+
+/* y[m][n] = sum_k x[m][k] * w[n][k]: the linear layer's weight is stored
+ * [out features][in features].  With x = the up-projected output
+ * [tokens][H * 128] (feature 128 h + d) and w = W_O it is the layer output;
+ * with x = the latent output [tokens][H * 512] (feature 512 h + c) and
+ * w = W_OV it is the same output through the fused weight. */
+int oracle_output_projection(int M, int K, int N, const double* x, const double* w, double* y) {
+  if (M < 0 || K < 1 || N < 1 || !x || !w || !y) return 1;
+#pragma omp parallel for schedule(static)
+  for (long long mn = 0; mn < (long long)M * N; ++mn) {
+    const int m = (int)(mn / N), n = (int)(mn % N);
+    double acc = 0.0;
+    for (int k = 0; k < K; ++k) acc += x[(size_t)m * K + k] * w[(size_t)n * K + k];
+    y[mn] = acc;
   }
   return 0;
 }

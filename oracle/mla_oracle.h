@@ -58,6 +58,15 @@ int oracle_cache_write(int B, int s, int max_seq_len, int fp8, const uint16_t* k
 int oracle_decode(const oracle_decode_args* a, int n_pairs, const int32_t* pairs, double* out,
                   double* probs);
 
+/* Latent output of the same steps before the up-projection, for the same
+ * pairs: olat double [n][C].  Returns 0 on success. */
+int oracle_decode_latent(const oracle_decode_args* a, int n_pairs, const int32_t* pairs,
+                         double* olat);
+
+/* y[m][n] = sum_k x[m][k] * w[n][k] in double (x [M][K], w [N][K], y [M][N]).
+ * Returns 0 on success. */
+int oracle_output_projection(int M, int K, int N, const double* x, const double* w, double* y);
+
 int oracle_num_threads(void);
 
 #ifdef __cplusplus

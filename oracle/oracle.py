@@ -52,6 +52,11 @@ def lib():
         L.oracle_decode.restype = ctypes.c_int
         L.oracle_decode.argtypes = [ctypes.POINTER(_DecodeArgs), ctypes.c_int, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p]
+        L.oracle_decode_latent.restype = ctypes.c_int
+        L.oracle_decode_latent.argtypes = [ctypes.POINTER(_DecodeArgs), ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.c_void_p]
+        L.oracle_output_projection.restype = ctypes.c_int
+        L.oracle_output_projection.argtypes = [ctypes.c_int] * 3 + [ctypes.c_void_p] * 3
         L.oracle_num_threads.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -140,18 +145,8 @@ def cache_write(kv_new, pe_new, start_pos, max_seq_len, fp8, kv_cache=None, kv_s
     return kv_cache, kv_scale, pe_cache
 
 
-def decode(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, softmax_scale, kv_scale=None,
-           topk_idx=None, pairs=None, want_probs=False):
-    """Oracle decode; returns out (float64) [B][H][128] for one query token,
-    [B][s][H][128] for s > 1, or [n_pairs][128] (+ probs).
-
-    q_nope [B][s][H][128], q_pe [B][s][H][64], wkv_b [H][256][512] (bf16);
-    kv_cache bf16 [B][T][512] or uint8 E4M3FN codes (then kv_scale fp32 [B][T][4]);
-    pe_cache bf16 [B][T][64]; cache_lens int32 [B]; topk_idx int32 [B][s][k] or None;
-    pairs: optional int array [n][2] of (q, h) to evaluate, q = b * s + i.
-    The s query tokens are the last s cached positions; token i sees rows
-    t < end_b - (s - 1 - i).
-    """
+def _decode_args(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, softmax_scale, kv_scale,
+                 topk_idx):
     qn = _np(q_nope, np.uint16)
     qp = _np(q_pe, np.uint16)
     w = _np(wkv_b, np.uint16)
@@ -174,14 +169,36 @@ def decode(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, softmax_scale, k
         assert ti.size == B * s * k
     args = _DecodeArgs(B, H, T, s, int(fp8), k, float(softmax_scale), _ptr(qn), _ptr(qp), _ptr(w),
                        _ptr(kv), _ptr(sc), _ptr(pe), _ptr(lens), _ptr(ti))
-    if pairs is not None:
-        pr = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
-        n = pr.shape[0]
-    else:
-        pr, n = None, B * s * H
+    keep = (qn, qp, w, kv, sc, pe, lens, ti)  # the arrays the pointers refer to
+    return args, keep, (B, s, H, T)
+
+
+def _pairs(pairs, n_all):
+    if pairs is None:
+        return None, n_all
+    pr = np.ascontiguousarray(np.asarray(pairs, dtype=np.int32).reshape(-1, 2))
+    return pr, pr.shape[0]
+
+
+def decode(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, softmax_scale, kv_scale=None,
+           topk_idx=None, pairs=None, want_probs=False):
+    """Oracle decode; returns out (float64) [B][H][128] for one query token,
+    [B][s][H][128] for s > 1, or [n_pairs][128] (+ probs).
+
+    q_nope [B][s][H][128], q_pe [B][s][H][64], wkv_b [H][256][512] (bf16);
+    kv_cache bf16 [B][T][512] or uint8 E4M3FN codes (then kv_scale fp32 [B][T][4]);
+    pe_cache bf16 [B][T][64]; cache_lens int32 [B]; topk_idx int32 [B][s][k] or None;
+    pairs: optional int array [n][2] of (q, h) to evaluate, q = b * s + i.
+    The s query tokens are the last s cached positions; token i sees rows
+    t < end_b - (s - 1 - i).
+    """
+    args, keep, (B, s, H, T) = _decode_args(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens,
+                                            softmax_scale, kv_scale, topk_idx)
+    pr, n = _pairs(pairs, B * s * H)
     out = np.zeros((n, D_V), np.float64)
     probs = np.zeros((n, T), np.float64) if want_probs else None
     rc = lib().oracle_decode(ctypes.byref(args), n, _ptr(pr), _ptr(out), _ptr(probs))
+    del keep
     if rc != 0:
         raise ValueError("oracle_decode rejected its arguments")
     if pairs is None:
@@ -189,3 +206,41 @@ def decode(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, softmax_scale, k
         if want_probs:
             probs = probs.reshape((B, H, T) if s == 1 else (B, s, H, T))
     return (out, probs) if want_probs else out
+
+
+def decode_latent(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, softmax_scale, kv_scale=None,
+                  topk_idx=None, pairs=None):
+    """The latent output of the decode before the value up-projection,
+    o[c] = sum_t p[t] c_KV[t, c] (float64): [B][s][H][512], or [n_pairs][512]."""
+    args, keep, (B, s, H, T) = _decode_args(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens,
+                                            softmax_scale, kv_scale, topk_idx)
+    pr, n = _pairs(pairs, B * s * H)
+    olat = np.zeros((n, C_LATENT), np.float64)
+    rc = lib().oracle_decode_latent(ctypes.byref(args), n, _ptr(pr), _ptr(olat))
+    del keep
+    if rc != 0:
+        raise ValueError("oracle_decode_latent rejected its arguments")
+    return olat.reshape(B, s, H, C_LATENT) if pairs is None else olat
+
+
+def output_projection(x, w):
+    """y[m][n] = sum_k x[m][k] w[n][k] in float64.  x: [..., K] (float64, or a
+    bf16 tensor), w: [N, K] (bf16 tensor or float array); returns [..., N]."""
+    def f64(a):
+        try:
+            import torch
+            if isinstance(a, torch.Tensor):
+                return a.detach().cpu().to(torch.float64).numpy()
+        except ImportError:
+            pass
+        return np.asarray(a, dtype=np.float64)
+    xa = np.ascontiguousarray(f64(x))
+    wa = np.ascontiguousarray(f64(w))
+    K = xa.shape[-1]
+    N = wa.shape[0]
+    assert wa.shape == (N, K)
+    M = xa.size // K
+    y = np.zeros(xa.shape[:-1] + (N,), np.float64)
+    if lib().oracle_output_projection(M, K, N, _ptr(xa), _ptr(wa), _ptr(y)) != 0:
+        raise ValueError("oracle_output_projection rejected its arguments")
+    return y

@@ -533,3 +533,77 @@ def test_multitoken_last_token_sees_the_whole_cache():
     ref = naive_mha(f64(x["q_nope"][:, s - 1:]), f64(x["q_pe"][:, s - 1:]), f64(x["wkv_b"]), f64(x["kv"]),
                     f64(x["pe"]), dense_sel(lens.numpy(), T), SCALE)
     assert rel(got[:, s - 1], ref) < 1e-12
+
+
+# ---------------------------------------------------------------- latent output and W_O / W_OV
+
+def test_latent_output_up_projects_to_naive_mha():
+    # the latent output o (before the value up-projection) times W_UV equals
+    # the expanded multi-head attention output (MLA article, section 4: the
+    # weights multiply the cached latents, W_UV comes after): dense ragged,
+    # top-k and FP8
+    for kw in (dict(ragged=(3, 24)), dict(topk=9), dict(fp8=True)):
+        w, x = tiny(2, 4, 24, seed=41, **kw)
+        if w.fp8:
+            codes, scales, pe = oracle.cache_write(x["kv"], x["pe"], torch.zeros(2, dtype=torch.int32),
+                                                   24, True)
+            lat, kvc = dequant_with_torch(codes, scales), codes
+        else:
+            scales, pe, lat, kvc = None, x["pe"], f64(x["kv"]), x["kv"]
+        olat = oracle.decode_latent(x["q_nope"], x["q_pe"], x["wkv_b"], kvc, pe, x["cache_lens"], SCALE,
+                                    kv_scale=scales, topk_idx=x["topk_idx"])[:, 0]       # [B,H,512]
+        if w.topk:
+            sel = np.zeros((2, 24), bool)
+            for b in range(2):
+                for i in x["topk_idx"][b, 0].tolist():
+                    if 0 <= i < int(x["cache_lens"][b]):
+                        sel[b, i] = True
+        else:
+            sel = dense_sel(x["cache_lens"].numpy(), 24)
+        ref = naive_mha(f64(x["q_nope"]), f64(x["q_pe"]), f64(x["wkv_b"]), lat, f64(x["pe"]), sel,
+                        SCALE)
+        w_uv = f64(x["wkv_b"])[:, 128:, :]                                              # [H,128,512]
+        got = np.einsum("hdc,bhc->bhd", w_uv, olat)
+        assert rel(got, ref) < 1e-12, kw
+
+
+def _w_ov(w_o, wkv_b):
+    """The fused weight of the MLA article's section 4, built here with numpy:
+    W_OV[:, 512 h : 512 h + 512] = W_O[:, 128 h : 128 h + 128] @ W_UV[h]."""
+    H = wkv_b.shape[0]
+    return np.concatenate([w_o[:, 128 * h:128 * h + 128] @ wkv_b[h, 128:, :] for h in range(H)], axis=1)
+
+
+def test_output_projection_identity_w_ov_equals_w_o_after_w_uv():
+    # W_OV o = W_O (W_UV o) for every token (MLA article, section 4 fusion,
+    # section 5 W_O after the up-projection), through the oracle on both sides
+    B, s, H, T, D = 2, 2, 4, 20, 48
+    x = multitoken_inputs(B, s, H, T, seed=42)
+    lens = torch.tensor([20, 13], dtype=torch.int32)
+    g = torch.Generator().manual_seed(43)
+    w_o = (torch.randn(D, H * 128, generator=g) / math.sqrt(H * 128)).to(torch.bfloat16)
+    out = oracle.decode(x["q_nope"], x["q_pe"], x["wkv_b"], x["kv"], x["pe"], lens, SCALE)      # [B,s,H,128]
+    olat = oracle.decode_latent(x["q_nope"], x["q_pe"], x["wkv_b"], x["kv"], x["pe"], lens, SCALE)
+    y_o = oracle.output_projection(out.reshape(B, s, H * 128), w_o)
+    w_ov = _w_ov(f64(w_o), f64(x["wkv_b"]))
+    y_ov = oracle.output_projection(olat.reshape(B, s, H * 512), w_ov)
+    assert y_o.shape == (B, s, D) and rel(y_ov, y_o) < 1e-12
+    # and against numpy's own product of the page's shapes
+    assert rel(y_o, out.reshape(B, s, H * 128) @ f64(w_o).T) < 1e-12
+
+
+def test_output_projection_closed_forms():
+    g = torch.Generator().manual_seed(44)
+    N, K = 7, 256
+    w = torch.randn(N, K, generator=g).to(torch.bfloat16)
+    wf = f64(w)
+    # one-hot inputs pick columns of the weight (feature k -> W[:, k])
+    for k in (0, 1, 127, 128, 255):
+        e = np.zeros((1, K))
+        e[0, k] = 1.0
+        assert np.array_equal(oracle.output_projection(e, w)[0], wf[:, k])
+    # all-ones input gives the row sums; scaling is linear
+    ones = np.ones((3, K))
+    assert np.allclose(oracle.output_projection(ones, w), np.tile(wf.sum(axis=1), (3, 1)), rtol=1e-14)
+    xr = np.random.default_rng(45).standard_normal((5, K))
+    assert rel(oracle.output_projection(2.5 * xr, w), 2.5 * oracle.output_projection(xr, w)) < 1e-14
