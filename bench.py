@@ -405,6 +405,90 @@ def measure(w, args, steps, warmup, mla, synth, torch, np, S=1):
     return res, x
 
 
+def measure_oproj(w, x, steps, warmup, mla, synth, torch, np):
+    """The step after the decode path, both ways the MLA article gives it, on
+    workload w's inputs (s = 1): (a) mla_decode (with its up-projection) then
+    mla_output_projection with W_O [d_model][H * 128]; (b) mla_decode_latent
+    then mla_output_projection with the offline-fused W_OV = W_O W_UV
+    [d_model][H * 512].  Each path is captured in a HIP graph and `steps`
+    replays are timed; the projection kernels are also timed alone with
+    dispatch-stamped events."""
+    dev = "cuda:0"
+    B, H, T = w.batch, w.heads, w.max_seq_len
+    D = synth.D_MODEL
+    w_o = synth.make_w_o(H, D, seed=w.seed + 500).to(dev)
+    wkv_b = x["wkv_b"].to(dev)
+    w_ov = torch.empty(D, H * 512, dtype=torch.bfloat16, device=dev)
+    for h in range(H):  # fp32 products of the bf16 weights, rounded once (setup, not timed)
+        w_ov[:, 512 * h:512 * h + 512] = (w_o[:, 128 * h:128 * h + 128].float()
+                                          @ wkv_b[h, 128:, :].float()).to(torch.bfloat16)
+    if w.fp8:
+        kv = torch.zeros(B, T, 512, dtype=torch.uint8, device=dev)
+        sc = torch.zeros(B, T, 4, dtype=torch.float32, device=dev)
+        pe = torch.zeros(B, T, 64, dtype=torch.bfloat16, device=dev)
+        mla.cache_write(x["kv"].to(dev), x["pe"].to(dev), torch.zeros(B, dtype=torch.int32, device=dev),
+                        kv, pe, kv_scale=sc)
+    else:
+        kv, sc, pe = x["kv"].to(dev), None, x["pe"].to(dev)
+    qn, qp, lens = x["q_nope"].to(dev), x["q_pe"].to(dev), x["cache_lens"].to(dev)
+    topk = None if x["topk_idx"] is None else x["topk_idx"].to(dev)
+    p = mla.make_params(B, H, T, 1 if w.fp8 else 0, topk=w.topk)
+    ws = torch.empty(mla.decode_workspace_size(p), dtype=torch.uint8, device=dev)
+    out = torch.empty(B, 1, H, 128, dtype=torch.bfloat16, device=dev)
+    lat = torch.empty(B, 1, H, 512, dtype=torch.bfloat16, device=dev)
+    y = torch.empty(B, 1, D, dtype=torch.bfloat16, device=dev)
+
+    def path_a(ev=None):
+        mla.decode(qn, qp, wkv_b, kv, pe, lens, kv_scale=sc, topk_idx=topk, out=out, workspace=ws)
+        mla.output_projection(out, w_o, mla.OPROJ_WO, y=y, trace_events=ev)
+
+    def path_b(ev=None):
+        mla.decode_latent(qn, qp, wkv_b, kv, pe, lens, kv_scale=sc, topk_idx=topk, o_lat=lat,
+                          workspace=ws)
+        mla.output_projection(lat, w_ov, mla.OPROJ_WOV, y=y, trace_events=ev)
+
+    res = {"d_model": D, "w_o_bytes": w_o.numel() * 2, "w_ov_bytes": w_ov.numel() * 2,
+           "workload": w.name}
+    hev = HipEvents()
+    for name, fn in (("w_o", path_a), ("w_ov", path_b)):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        res[f"path_{name}_us"] = 1e6 * (time.perf_counter() - t0) / steps
+        ev = hev.create(2 * steps)
+        arrs = [(ctypes.c_void_p * 2)(*ev[2 * i: 2 * i + 2]) for i in range(steps)]
+        torch.cuda._sleep(int(2e8))
+        for i in range(steps):
+            fn(ev=ctypes.addressof(arrs[i]))
+        torch.cuda.synchronize()
+        kus = 1e3 * float(np.mean([hev.elapsed_ms(ev[2 * i], ev[2 * i + 1]) for i in range(steps)]))
+        hev.destroy(ev)
+        res[f"oproj_{name}_kernel_us"] = kus
+        res[f"oproj_{name}_gbps"] = res[f"{name}_bytes"] / (kus * 1e-6) / 1e9
+        del g
+    res["w_ov_path_over_w_o_path"] = res["path_w_ov_us"] / res["path_w_o_us"]
+    del w_o, w_ov, kv, sc, pe, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -426,6 +510,9 @@ def main():
                     help="mla_cache_write then mla_decode instead of mla_decode_step")
     ap.add_argument("--no-stream-probe", action="store_true",
                     help="skip the read-only measurement of attainable HBM bandwidth")
+    ap.add_argument("--no-oproj", action="store_true",
+                    help="skip the output-projection comparison (W_O after the up-projection "
+                         "against the fused W_OV on the latent output)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run 5 plain device copies of BYTES bytes (reference for the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -472,6 +559,11 @@ def main():
             "step_bound": r["step_bound"], "kernel_avg_us": r["kernel_avg_us"],
             "roofline": r["roofline"],
         }
+    oproj = None
+    if not args.no_oproj and S == 1:
+        print(f"bench: output projection of {w.name}: W_O path and fused W_OV path", file=sys.stderr,
+              flush=True)
+        oproj = measure_oproj(w, x, args.extra_steps, args.extra_warmup, mla, synth, torch, np)
     stream_gbps = None if args.no_stream_probe else stream_probe(torch)
     for r in [head] + list(configs.values()):
         roof = r["roofline"]
@@ -505,6 +597,7 @@ def main():
         "kernel_timing": "dispatch-stamped HIP events, eager pass of the same K steps",
         "roofline": head["roofline"],
         "configs": configs,
+        "output_projection": oproj,
     }
     if not args.no_cpu_baseline:
         import oracle

@@ -199,6 +199,43 @@ mla_status mla_decode_step(const mla_params* p, const void* kv_new, const void* 
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * mla_decode_latent -- mla_decode without its last step: the output is the
+ * latent attention output of each head, before the value up-projection.
+ *
+ * Steps 1-4 of mla_decode (the MLA article, section 4: the attention weights
+ * multiply the cached 512-wide latents directly, and W_UV is applied after,
+ * or fused offline into the output projection as W_OV = W_O W_UV):
+ *   o_lat[b,i,h,c] = sum_t p[t] * c_KV[b,t,c]
+ *   o_lat      bf16 [B][s][H][512] (replaces `out`)
+ * Every other argument, the checks, the workspace size and the errors are
+ * those of mla_decode (trace events: kernels 0-2; no kernel 3 is launched).
+ */
+mla_status mla_decode_latent(const mla_params* p, const void* q_nope, const void* q_pe,
+                             const void* wkv_b, const void* kv_cache, const float* kv_scale,
+                             const void* pe_cache, const int32_t* cache_lens, const int32_t* topk_idx,
+                             void* o_lat, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_output_projection -- the layer's output projection after the decode,
+ * for the batch * seqlen_q query tokens m (MLA article, section 5: the
+ * heads' outputs, concatenated, go through W_O; section 4: W_UV fused into it
+ * offline, W_OV[:, 512 h .. 512 h + 511] = W_O[:, 128 h .. 128 h + 127] W_UV[h]):
+ *   y[m][n] = sum_k x[m][k] * w[n][k],  n < d_model
+ *   kind MLA_OPROJ_WO:  x = mla_decode's out [B][s][H][128] (k = 128 h + d),
+ *                       w = W_O bf16 [d_model][H * 128]
+ *   kind MLA_OPROJ_WOV: x = mla_decode_latent's o_lat [B][s][H][512]
+ *                       (k = 512 h + c), w = W_OV bf16 [d_model][H * 512]
+ *   y          bf16 [B][s][d_model] (fp32 accumulation, one rounding)
+ * p gives batch, seqlen_q and num_heads (the other fields are checked as for
+ * mla_decode); 1 <= d_model <= 2^20.  No workspace; trace events 0 and 1
+ * time its one kernel.  Deterministic: the same inputs give the same bits.
+ */
+#define MLA_OPROJ_WO 0
+#define MLA_OPROJ_WOV 1
+mla_status mla_output_projection(const mla_params* p, int32_t d_model, int32_t kind, const void* x,
+                                 const void* w, void* y, void* stream);
+
+/*
  * mla_decode_noalloc -- mla_decode without a workspace argument, for callers
  * that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc).

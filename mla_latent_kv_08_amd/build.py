@@ -11,7 +11,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["mla_abi.hip", "mla_cache_write.hip", "mla_decode.hip"]
+SOURCES = ["mla_abi.hip", "mla_cache_write.hip", "mla_decode.hip", "mla_oproj.hip"]
 # the benchmark's HBM read-rate probe: a library of its own, not part of the ABI
 PROBE_LIB = os.path.join(PKG, "libhbmprobe.so")
 PROBE_SOURCE = "hbm_probe.hip"

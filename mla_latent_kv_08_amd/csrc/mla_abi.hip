@@ -242,6 +242,46 @@ mla_status mla_decode_step(const mla_params* p, const void* kv_new, const void* 
 
 extern "C" {
 
+mla_status mla_decode_latent(const mla_params* p, const void* q_nope, const void* q_pe,
+                             const void* wkv_b, const void* kv_cache, const float* kv_scale,
+                             const void* pe_cache, const int32_t* cache_lens, const int32_t* topk_idx,
+                             void* o_lat, void* workspace, size_t workspace_bytes, void* stream) {
+  mla::DecodePlan plan;
+  mla_status st = check_decode(p, q_nope, q_pe, wkv_b, kv_cache, kv_scale, pe_cache, cache_lens,
+                               topk_idx, o_lat, workspace, workspace_bytes, &plan);
+  if (st != MLA_OK || p->batch == 0) return st == MLA_OK ? ok() : st;
+  mla::DecodeArgs d{q_nope, q_pe, wkv_b, kv_cache, kv_scale, pe_cache, cache_lens, topk_idx, nullptr, workspace};
+  const hipError_t e = mla::launch_decode(*p, d, nullptr, (hipStream_t)stream, o_lat);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "HIP: %s", hipGetErrorString(e));
+  return ok();
+}
+
+mla_status mla_output_projection(const mla_params* p, int32_t d_model, int32_t kind, const void* x,
+                                 const void* w, void* y, void* stream) {
+  mla_status st = check_params(p);
+  if (st != MLA_OK) return st;
+  st = check_decode_shape(p);
+  if (st != MLA_OK) return st;
+  if (kind != MLA_OPROJ_WO && kind != MLA_OPROJ_WOV)
+    return fail(MLA_ERR_INVALID_ARG, "unknown output projection kind %d", kind);
+  if (d_model < 1 || d_model > (1 << 20))
+    return fail(MLA_ERR_INVALID_ARG, "d_model = %d outside 1..2^20", d_model);
+  if (p->batch == 0) return ok();
+  if (!x || !w || !y) return fail(MLA_ERR_INVALID_ARG, "a required tensor pointer is NULL");
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16))
+    return fail(MLA_ERR_INVALID_ARG, "bf16 tensors must be 16-byte aligned");
+  const int M = p->batch * p->seqlen_q;
+  const int K = p->num_heads * (kind == MLA_OPROJ_WO ? MLA_V_HEAD_DIM : MLA_KV_LORA_RANK);
+  const hipError_t e = mla::launch_output_projection(x, w, y, M, d_model, K, (hipStream_t)stream,
+                                                     (hipEvent_t const*)p->trace_events);
+  if (e != hipSuccess) return fail(MLA_ERR_HIP, "HIP: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
+
+extern "C" {
+
 mla_status mla_decode_noalloc(const mla_params* p, const void* q_nope, const void* q_pe,
                               const void* wkv_b, const void* kv_cache, const float* kv_scale,
                               const void* pe_cache, const int32_t* cache_lens,

@@ -1461,14 +1461,14 @@ __global__ __launch_bounds__(64) void uproj_kernel(const uint16_t* __restrict__ 
 
 // ---------------------------------------------------------------------------
 hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWriteArgs* write,
-                         hipStream_t stream) {
+                         hipStream_t stream, void* latent_out) {
   const DecodePlan plan = make_decode_plan(p);
   const int s = p.seqlen_q, B = p.batch * s, H = p.num_heads;  // B: query tokens
   char* ws = (char*)d.workspace;
   uint16_t* qt = (uint16_t*)(ws + plan.off_qt);
   uint16_t* part_o = (uint16_t*)(ws + plan.off_part_o);
   float* part_ml = (float*)(ws + plan.off_part_ml);
-  uint16_t* olat = (uint16_t*)(ws + plan.off_olat);
+  uint16_t* olat = latent_out ? (uint16_t*)latent_out : (uint16_t*)(ws + plan.off_olat);
   hipEvent_t* ev = (hipEvent_t*)p.trace_events;
   auto evk = [&](int k) -> hipEvent_t const* { return ev ? ev + 2 * k : nullptr; };
   hipError_t err;
@@ -1535,6 +1535,7 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
                       (const uint16_t*)part_o, (const float*)part_ml, (const int32_t*)wcum, olat, H,
                       plan.heads_padded);
   if (err != hipSuccess) return err;
+  if (latent_out) return hipSuccess;  // the caller takes the latent output
 
   err = launch_kernel(uproj_kernel, dim3(H, 4), dim3(64), stream, evk(3), (const uint16_t*)olat,
                       (const uint16_t*)d.wkv_b, (uint16_t*)d.out, B, H);

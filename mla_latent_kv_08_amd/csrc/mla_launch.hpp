@@ -35,8 +35,15 @@ struct CacheWriteArgs {
 
 // With `write` non-null (the fused decode step) the new row of each sequence is
 // stored at position cache_lens[b] - 1 before the attention reads the caches.
+// With `latent_out` non-null the combine writes the latent output
+// [B][s][H][512] there and the up-projection is not launched (d.out unused).
 hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWriteArgs* write,
-                         hipStream_t stream);
+                         hipStream_t stream, void* latent_out = nullptr);
+
+// y[m][n] = sum_k x[m][k] w[n][k], bf16 in and out (fp32 accumulation);
+// K a multiple of 64.
+hipError_t launch_output_projection(const void* x, const void* w, void* y, int M, int N, int K,
+                                    hipStream_t stream, hipEvent_t const* ev);
 
 // Launch `kernel` on `stream` and return the launch's own status (not the
 // thread's last error, which an earlier unrelated HIP call may have left).

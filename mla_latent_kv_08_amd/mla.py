@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libmla.so")
 C_LATENT, R_ROPE, D_NOPE, D_V = 512, 64, 128, 128
 KV_BF16, KV_FP8_E4M3_B128 = 0, 1
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MLA_NOALLOC_SCRATCH_BYTES
+OPROJ_WO, OPROJ_WOV = 0, 1
 DEFAULT_SOFTMAX_SCALE = 1.0 / math.sqrt(D_NOPE + R_ROPE)
 
 STATUS = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
@@ -59,6 +60,10 @@ def _load():
     L.mla_decode.argtypes = [P] + [vp] * 10 + [ctypes.c_size_t, vp]
     L.mla_decode_step.restype = ctypes.c_int
     L.mla_decode_step.argtypes = [P] + [vp] * 12 + [ctypes.c_size_t, vp]
+    L.mla_decode_latent.restype = ctypes.c_int
+    L.mla_decode_latent.argtypes = [P] + [vp] * 10 + [ctypes.c_size_t, vp]
+    L.mla_output_projection.restype = ctypes.c_int
+    L.mla_output_projection.argtypes = [P, ctypes.c_int32, ctypes.c_int32, vp, vp, vp, vp]
     L.mla_decode_noalloc.restype = ctypes.c_int
     L.mla_decode_noalloc.argtypes = [P] + [vp] * 10
     L.mla_status_string.restype = ctypes.c_char_p
@@ -172,6 +177,45 @@ def decode_step(kv_new, pe_new, q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_l
                                _ptr(pe_cache), _ptr(cache_lens), _ptr(topk_idx), _ptr(out),
                                _ptr(workspace), workspace.numel(), _stream(stream)))
     return out
+
+
+def decode_latent(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, kv_scale=None, topk_idx=None,
+                  o_lat=None, workspace=None, softmax_scale=DEFAULT_SOFTMAX_SCALE, stream=None,
+                  trace_events=None):
+    """mla_decode_latent: returns the latent output o_lat [B,s,H,512] bf16 (the
+    attention output before the value up-projection); arguments as for decode."""
+    _dev(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, kv_scale, topk_idx, o_lat, workspace)
+    B, s, H = q_nope.shape[0], q_nope.shape[1], q_nope.shape[2]
+    fp8 = kv_scale is not None
+    k = 0 if topk_idx is None else topk_idx.shape[-1]
+    p = make_params(B, H, kv_cache.shape[1], KV_FP8_E4M3_B128 if fp8 else KV_BF16, topk=k,
+                    seqlen_q=s, softmax_scale=softmax_scale, trace_events=trace_events)
+    if o_lat is None:
+        o_lat = torch.empty(B, s, H, C_LATENT, dtype=torch.bfloat16, device=q_nope.device)
+    if workspace is None:
+        workspace = torch.empty(max(decode_workspace_size(p), 16), dtype=torch.uint8,
+                                device=q_nope.device)
+    _check(lib.mla_decode_latent(ctypes.byref(p), _ptr(q_nope), _ptr(q_pe), _ptr(wkv_b), _ptr(kv_cache),
+                                 _ptr(kv_scale), _ptr(pe_cache), _ptr(cache_lens), _ptr(topk_idx),
+                                 _ptr(o_lat), _ptr(workspace), workspace.numel(), _stream(stream)))
+    return o_lat
+
+
+def output_projection(x, w, kind, y=None, stream=None, trace_events=None):
+    """mla_output_projection: y [B,s,d_model] bf16 = x [B,s,H,F] . w[d_model, H*F]^T with
+    (kind, F) = (OPROJ_WO, 128) for W_O after decode, or (OPROJ_WOV, 512) for the fused
+    W_OV after decode_latent."""
+    _dev(x, w, y)
+    B, s, H, F = x.shape
+    if F != (D_V if kind == OPROJ_WO else C_LATENT) or tuple(w.shape[1:]) != (H * F,):
+        raise ValueError("x and w do not match the projection kind")
+    d_model = w.shape[0]
+    p = make_params(B, H, 1, seqlen_q=s, trace_events=trace_events)
+    if y is None:
+        y = torch.empty(B, s, d_model, dtype=torch.bfloat16, device=x.device)
+    _check(lib.mla_output_projection(ctypes.byref(p), d_model, kind, _ptr(x), _ptr(w), _ptr(y),
+                                     _stream(stream)))
+    return y
 
 
 def decode_noalloc(q_nope, q_pe, wkv_b, kv_cache, pe_cache, cache_lens, out, kv_scale=None,

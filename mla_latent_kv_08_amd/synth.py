@@ -124,3 +124,16 @@ def add_query_tokens(x: dict, s: int, seed: int) -> dict:
     if x["topk_idx"] is not None:
         y["topk_idx"] = x["topk_idx"].expand(B, s, x["topk_idx"].shape[-1]).contiguous()
     return y
+
+
+D_MODEL = 7168  # DeepSeek-V3 hidden size: the output projection's width
+
+
+def make_w_o(heads: int, d_model: int = D_MODEL, seed: int = 0) -> torch.Tensor:
+    """Seeded synthetic output projection W_O, bf16 [d_model][heads * 128]
+    (a linear layer's weight: [out features][in features]), N(0, variance
+    1/(heads * 128)) so that unit-variance head outputs give unit-variance
+    layer outputs."""
+    g = torch.Generator().manual_seed(seed)
+    k = heads * D_V
+    return (torch.randn(d_model, k, generator=g) / math.sqrt(k)).to(torch.bfloat16)
