@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <string.h>
 
 #include <atomic>
 #include <mutex>
@@ -77,7 +78,11 @@ mla_status check_decode_shape(const mla_params* p) {
 extern "C" {
 
 const char* mla_status_string(mla_status s) {
-  switch (s) {
+  // A C caller may pass any int: read the argument's bits as an int, since
+  // loading an out-of-range value as the C++ enum would be undefined.
+  int v;
+  memcpy(&v, &s, sizeof v);
+  switch (v) {
     case MLA_OK: return "MLA_OK";
     case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: invalid argument";
     case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: not implemented by this build";

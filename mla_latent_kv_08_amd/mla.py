@@ -12,7 +12,9 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmla.so")
+# MLA_LIB overrides the library path (the sanitizer test loads a host-only,
+# ASan/UBSan build of the same sources through it)
+LIB_PATH = os.environ.get("MLA_LIB") or os.path.join(_PKG, "libmla.so")
 
 C_LATENT, R_ROPE, D_NOPE, D_V = 512, 64, 128, 128
 KV_BF16, KV_FP8_E4M3_B128 = 0, 1

@@ -30,7 +30,7 @@ class _DecodeArgs(ctypes.Structure):
 def lib():
     global _lib
     if _lib is None:
-        path = _build.LIB
+        path = os.environ.get("ORACLE_LIB") or _build.LIB  # ORACLE_LIB: e.g. a sanitizer build
         if not os.path.exists(path):
             _build.build()
         L = ctypes.CDLL(path)
