@@ -489,23 +489,6 @@ __device__ __forceinline__ int tile_off(int t, int ch) { return t * kQK + ((ch ^
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(lds_void*)p;
-}
-
-// 16-byte global -> LDS copy for each lane: lane l's 16 bytes from `src` land
-// at LDS byte address base + OFF + 16 l (base must be wave-uniform).  Written as
-// inline asm so the compiler's wait-count tracking does not treat every later
-// LDS read as possibly depending on it; completion is awaited explicitly with
-// s_waitcnt vmcnt before the workgroup barrier that publishes the tile.
-template <int OFF>
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t base) {
-  asm volatile("s_add_u32 m0, %1, %2\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base), "i"(OFF)
-               : "memory", "m0", "scc");
-}
 
 // 4-byte global -> LDS copy for each lane (lane l's dword at base + OFF + 4 l),
 // issued after `dep` is available.
@@ -548,8 +531,6 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// s_waitcnt vmcnt(n) leaving the other counters unconstrained.
-#define MLA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
 // Workgroup barrier that publishes this wave's LDS writes but, unlike
 // __syncthreads, does not wait for its global loads still in flight.
 #define MLA_LDS_BARRIER()                                           \

@@ -98,6 +98,27 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void*)p;
+}
+
+// 16-byte global -> LDS copy for each lane: lane l's 16 bytes from `src` land
+// at LDS byte address base + OFF + 16 l (base must be wave-uniform).  Written as
+// inline asm so the compiler's wait-count tracking does not treat every later
+// LDS read as possibly depending on it; completion is awaited explicitly with
+// s_waitcnt vmcnt (before a barrier when other waves read the data).
+template <int OFF>
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t base) {
+  asm volatile("s_add_u32 m0, %1, %2\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base), "i"(OFF)
+               : "memory", "m0", "scc");
+}
+
+// s_waitcnt vmcnt(n) leaving the other counters unconstrained.
+#define MLA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

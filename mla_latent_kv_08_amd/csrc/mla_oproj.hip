@@ -13,53 +13,88 @@
 
 namespace mla {
 
-constexpr int kOpWaves = 8;      // waves per workgroup (two per SIMD)
-constexpr int kOpChunk = 64;     // k per chunk: four 16-wide MFMA steps
-constexpr int kOpUnroll = 4;     // chunks whose loads a wave issues before their MFMAs
+constexpr int kOpWaves = 4;      // waves per workgroup, one per SIMD
+constexpr int kOpKT = 64;        // k per tile: four 16-wide MFMA steps, 128 bytes per row
+constexpr int kOpSlots = 4;      // tiles in each wave's ring (three in flight)
+constexpr int kOpOperand = 32 * kOpKT * 2;   // 4 KB: 32 rows x 64 k, bf16
+constexpr int kOpSlot = 2 * kOpOperand;      // w tile then x tile
 
-// grid (ceil(N / 32), ceil(M / 32)), 512 threads.  Workgroup (i, j) computes
-// the 32 x 32 block y[32 j ..][32 i ..]: wave w takes the k chunks w, w + 8,
-// ... and accumulates A = w rows (lane l: row 32 i + l % 32, 8 consecutive k
-// at 16 step + 8 (l / 32)) times B = x rows (the same k of token 32 j + l %
-// 32) in one 32 x 32 block (D[n][m]); the eight partial blocks are summed in
-// LDS and rounded to bf16 once.  K is a multiple of 64; rows past N and
-// tokens past M read the last row instead and are not stored.
+// grid (ceil(N / 32), ceil(M / 32)), 256 threads.  Workgroup (i, j) computes
+// the 32 x 32 block y[32 j ..][32 i ..].  The k range is cut into tiles of 64;
+// wave v takes tiles v, v + 4, ... and streams each one (32 rows of w, 32
+// tokens of x) into its own ring of LDS slots with direct-to-LDS loads, three
+// tiles ahead: every 1 KB load covers 8 rows x 128 contiguous bytes.  In LDS a
+// row's 16-byte chunk c sits at c ^ ((row >> 1) & 7), so the MFMA operand
+// reads (16 rows per LDS cycle, one chunk each) hit distinct banks.  Per
+// tile: four 32x32x16 MFMAs with A = w rows (lane l: row l % 32, 8 k at
+// 16 step + 8 (l / 32)) and B = x rows (the same k of token l % 32) into
+// one 32 x 32 block D[n][m].  No wave waits for another until the four
+// partial blocks are summed in LDS and rounded to bf16 once.  K is a multiple
+// of 64; rows past N and tokens past M read the last row and are not stored.
 __global__ __launch_bounds__(64 * kOpWaves) void oproj_kernel(const uint16_t* __restrict__ x,
                                                               const uint16_t* __restrict__ w,
                                                               uint16_t* __restrict__ y, int M, int N,
                                                               int K) {
-  __shared__ float red[kOpWaves][16][64];
+  __shared__ __attribute__((aligned(16))) char lds[kOpWaves][kOpSlots][kOpSlot];  // 128 KB
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n0 = blockIdx.x * 32, m0 = blockIdx.y * 32;
-  const int r = lane & 31, g = lane >> 5;
-  const int wrow = min(n0 + r, N - 1), xrow = min(m0 + r, M - 1);
-  const uint16_t* wp = w + (size_t)wrow * K + 8 * g;
-  const uint16_t* xp = x + (size_t)xrow * K + 8 * g;
-  const int nc = K / kOpChunk;
-  f32x16 acc = {};
-  for (int c0 = wave; c0 < nc; c0 += kOpWaves * kOpUnroll) {
-    u32x4 a[kOpUnroll][4], b[kOpUnroll][4];
+  const int nt = K / kOpKT;
+  const int mine = nt > wave ? (nt - wave + kOpWaves - 1) / kOpWaves : 0;  // tiles of this wave
+  // Load q (0..3) of an operand tile covers rows 8 q .. 8 q + 7: lane l takes
+  // row 8 q + l / 8 and stores LDS chunk l % 8, i.e. global chunk
+  // (l % 8) ^ ((row >> 1) & 7) of that row.
+  const int lr = lane >> 3, lc = lane & 7;
+  const uint16_t* wsrc[4];
+  const uint16_t* xsrc[4];
 #pragma unroll
-    for (int u = 0; u < kOpUnroll; ++u) {
-      const int c = c0 + kOpWaves * u;
-      if (c < nc) {  // wave-uniform
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          a[u][s] = __builtin_nontemporal_load((const u32x4*)(wp + (size_t)c * kOpChunk + 16 * s));
-          b[u][s] = *(const u32x4*)(xp + (size_t)c * kOpChunk + 16 * s);
-        }
-      } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) a[u][s] = b[u][s] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kOpUnroll; ++u) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) acc = mfma32(a[u][s], b[u][s], acc);
-    }
+  for (int q = 0; q < 4; ++q) {
+    const int r = 8 * q + lr, gc = lc ^ ((r >> 1) & 7);
+    wsrc[q] = w + (size_t)min(n0 + r, N - 1) * K + 8 * gc;
+    xsrc[q] = x + (size_t)min(m0 + r, M - 1) * K + 8 * gc;
   }
+  auto issue = [&](int i) {  // the wave's i-th tile (global tile wave + 4 i) into slot i % 4
+    const size_t k0 = (size_t)(wave + kOpWaves * i) * kOpKT;
+    uint32_t base = lds_addr(lds[wave][i % kOpSlots]);
+    base = __builtin_amdgcn_readfirstlane(base);
+    lds_dma16<0>(wsrc[0] + k0, base);
+    lds_dma16<1024>(wsrc[1] + k0, base);
+    lds_dma16<2048>(wsrc[2] + k0, base);
+    lds_dma16<3072>(wsrc[3] + k0, base);
+    lds_dma16<kOpOperand>(xsrc[0] + k0, base);
+    lds_dma16<kOpOperand + 1024>(xsrc[1] + k0, base);
+    lds_dma16<kOpOperand + 2048>(xsrc[2] + k0, base);
+    lds_dma16<kOpOperand + 3072>(xsrc[3] + k0, base);
+  };
+  // operand read offsets (bytes in a slot) of the four k-steps
+  const int r = lane & 31, g = lane >> 5;
+  int roff[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) roff[st] = r * (kOpKT * 2) + (((2 * st + g) ^ ((r >> 1) & 7)) << 4);
+
+  f32x16 acc = {};
+  const int pre = mine < kOpSlots - 1 ? mine : kOpSlots - 1;
+  for (int i = 0; i < pre; ++i) issue(i);
+  for (int i = 0; i < mine; ++i) {
+    // tile i has landed once at most the loads of the tiles issued after it remain
+    const int after = min(mine - 1, i + kOpSlots - 2) - i;  // 0, 1 or 2 tiles
+    if (after >= 2) MLA_WAIT_VMCNT(16);
+    else if (after == 1) MLA_WAIT_VMCNT(8);
+    else MLA_WAIT_VMCNT(0);
+    const char* slot = lds[wave][i % kOpSlots];
+    u32x4 a[4], b[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      a[st] = *(const u32x4*)(slot + roff[st]);
+      b[st] = *(const u32x4*)(slot + kOpOperand + roff[st]);
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) acc = mfma32(a[st], b[st], acc);
+    // the slot refilled next held tile i - 1, whose operands are in registers
+    if (i + kOpSlots - 1 < mine) issue(i + kOpSlots - 1);
+  }
+  __syncthreads();  // every wave's ring is drained and read: reuse the LDS
+  float(*red)[16][64] = (float(*)[16][64])lds;
 #pragma unroll
   for (int e = 0; e < 16; ++e) red[wave][e][lane] = acc[e];
   __syncthreads();
