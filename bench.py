@@ -300,6 +300,13 @@ def measure(w, args, steps, warmup, mla, synth, torch, np, S=1):
         step(mla, reps[i % R], shared, out, ws)
     torch.cuda.synchronize()
 
+    # G consecutive steps per captured graph (as a model captures its layers
+    # together), G dividing `steps`; step t uses replica t % R, so graph k of
+    # L = lcm(G, R) / G distinct graphs covers the steps kG .. kG + G - 1
+    G = args.graph_steps or max(d for d in range(1, 17) if steps % d == 0)
+    if steps % G:
+        raise SystemExit(f"--graph-steps {G} does not divide {steps} steps")
+    L = R // math.gcd(G, R)
     graphs = []
     if not args.eager:
         side = torch.cuda.Stream()
@@ -308,21 +315,22 @@ def measure(w, args, steps, warmup, mla, synth, torch, np, S=1):
             step(mla, reps[0], shared, out, ws)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        for r in range(R):
+        for k in range(L):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                step(mla, reps[r], shared, out, ws)
+                for i in range(G):
+                    step(mla, reps[(k * G + i) % R], shared, out, ws)
             graphs.append(g)
-        for i in range(warmup):
-            graphs[i % R].replay()
+        for i in range(max(1, warmup // G)):
+            graphs[i % L].replay()
         torch.cuda.synchronize()
 
     # ---- timed region: exactly `steps` steps
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     if graphs:
-        for i in range(steps):
-            graphs[i % R].replay()
+        for k in range(steps // G):
+            graphs[k % L].replay()
     else:
         for i in range(steps):
             step(mla, reps[i % R], shared, out, ws)
@@ -387,7 +395,7 @@ def measure(w, args, steps, warmup, mla, synth, torch, np, S=1):
             "kv_cache": "fp8_e4m3_block128" if w.fp8 else "bf16",
             "selection": (f"top-{k}" if k else ("ragged U{%d..%d}" % w.ragged if w.ragged else "dense")),
             "rows_per_step": n_rows, "replicas": R,
-            "launch": "eager" if args.eager else "hip graph replay",
+            "launch": "eager" if args.eager else f"hip graph replay, {G} steps per graph",
             "entry": "mla_decode_step" if FUSED else "mla_cache_write + mla_decode",
         },
         "latent_cache_gbps": n_rows * row_bytes / step_s / 1e9,
@@ -503,6 +511,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true", help="time eager launches, not graph replay")
+    ap.add_argument("--graph-steps", type=int, default=0,
+                    help="steps captured per HIP graph (0: the largest divisor of the step count up to 16)")
     ap.add_argument("--seqlen-q", type=int, default=1,
                     help="query tokens per sequence (the last s cached positions; token i sees "
                          "the rows up to its own)")
