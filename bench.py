@@ -15,8 +15,9 @@ sequences of 1024..16384 rows (about 390 MB per step).  The other H = 128
 workloads (B = 1 at T = 4096, the FP8 cache at T = 32768, top-2048 of 65536)
 are timed in the same run with fewer steps and reported under "configs".
 
-Timing: each replica's step is captured once in a HIP graph; the timed region
-replays K steps, bracketed by torch.cuda.synchronize().  Per-kernel durations
+Timing: G consecutive steps (rotating over the replicas) are captured in one
+HIP graph, as a model captures its layers together; the timed region replays
+exactly K steps (K / G graph launches), bracketed by torch.cuda.synchronize().  Per-kernel durations
 come from a second pass of K eager steps in which the library launches every
 kernel with start/end HIP events stamped by the dispatch itself (the
 mla_params trace_events hook), i.e. the same kernel start and end times a
