@@ -40,7 +40,9 @@
 extern "C" {
 #endif
 
-#define MLA_ABI_VERSION 1
+/* 2: adds mla_decode_latent, mla_output_projection and mla_decode_noalloc;
+ * the entry points and mla_params of version 1 are unchanged. */
+#define MLA_ABI_VERSION 2
 
 /* Fixed widths of the DeepSeek-V3 MLA layer (checked in mla_params). */
 #define MLA_KV_LORA_RANK 512 /* latent width C */

@@ -30,10 +30,11 @@ def declared_functions():
 def test_exports_every_declared_symbol(m):
     names = declared_functions()
     assert {"mla_cache_write", "mla_decode", "mla_decode_step", "mla_decode_workspace_size",
+            "mla_decode_latent", "mla_output_projection", "mla_decode_noalloc",
             "mla_status_string", "mla_last_error", "mla_abi_version"} <= set(names)
     for n in names:
         assert hasattr(m.lib, n), n
-    assert m.lib.mla_abi_version() == 1
+    assert m.lib.mla_abi_version() == 2
 
 
 def test_params_struct_matches_header(m):
