@@ -63,3 +63,35 @@ def test_noalloc_fp8_topk_then_smaller_dense():
     _case(m, synth.Workload("na3", 4, 128, 2500, fp8=True, topk=600, outlier_frac=0.01,
                             outlier_mult=20.0, seed=93), "fp8 top-k")
     _case(m, synth.Workload("na4", 1, 16, 256, seed=94), "tiny dense")
+
+
+def test_noalloc_in_a_captured_graph():
+    """The use it is for: recorded into a HIP graph (after one eager call, which
+    looks up the scratch address), replayed several times with eager work in
+    between, every replay bit for bit equal to mla_decode's output."""
+    from mla_latent_kv_08_amd import mla as m
+    w = synth.Workload("na5", 3, 128, 1500, ragged=(1, 1500), seed=95)
+    x = synth.make_inputs(w)
+    print(f"[noalloc graph] B={w.batch} H={w.heads} T={w.max_seq_len}", flush=True)
+    d = {k: (None if v is None else v.to(DEV).contiguous()) for k, v in x.items()}
+    args = (d["q_nope"], d["q_pe"], d["wkv_b"], d["kv"], d["pe"], d["cache_lens"])
+    ref = m.decode(*args)
+    out = torch.zeros_like(ref)
+    m.decode_noalloc(*args, out)  # eager first call on this device
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            m.decode_noalloc(*args, out, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.zero_()
+        m.decode(*args)  # eager work between replays (its own workspace)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), rep
