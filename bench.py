@@ -517,6 +517,9 @@ def main():
     ap.add_argument("--seqlen-q", type=int, default=1,
                     help="query tokens per sequence (the last s cached positions; token i sees "
                          "the rows up to its own)")
+    ap.add_argument("--heads", type=int, default=0,
+                    help="query heads instead of the workload's (e.g. 16: one GPU's share of 128 "
+                         "heads on 8); names the workload <name>_h<heads>")
     ap.add_argument("--unfused", action="store_true",
                     help="mla_cache_write then mla_decode instead of mla_decode_step")
     ap.add_argument("--no-stream-probe", action="store_true",
@@ -551,6 +554,8 @@ def main():
     from mla_latent_kv_08_amd import mla, synth
 
     w = synth.WORKLOADS[args.workload]
+    if args.heads and args.heads != w.heads:
+        w = synth.scaled(w, heads=args.heads, name=f"{w.name}_h{args.heads}")
     S = args.seqlen_q
     print(f"bench: {w.name} s={S}: {args.warmup} warmup + {args.steps} timed steps", file=sys.stderr,
           flush=True)

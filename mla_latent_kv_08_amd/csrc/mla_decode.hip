@@ -302,28 +302,33 @@ __device__ __forceinline__ void write_new_rows(const RowWrite& rw, const int32_t
 }
 
 // ---------------------------------------------------------------------------
-// absorb: grid (heads_padded + 1 + writer columns, 4 column blocks of 128,
-// query-token ranges), 256 threads.  B counts query tokens (batch x s).
-// Workgroup (heads_padded, 0, 0) computes the attention work plan instead; in
+// absorb: grid (Hx + 1 + writer columns, 4 column blocks of 128, query-token
+// ranges), 256 threads, Hx = H + the padding rows of a work item.  B counts
+// query tokens (batch x s); work item it holds the ps tokens it ps .. + ps - 1
+// (ps = 1, or s when a sequence's tokens share their attention work), whose
+// query rows are packed as row i H + h for token i and head h.
+// Workgroup (Hx, 0, 0) computes the attention work plan instead; in
 // the fused step the workgroups of the writer columns (z = 0) store the new
 // cache rows of every sequence at positions cache_lens[b] - s .. - 1 (before
 // the attention kernel, which is launched after this one, reads the caches).
 //
 // Head h, columns 128y..128y+127: the W_UK slice (128 d x 128 c) is staged in
 // LDS and held as MFMA B fragments, wave w taking 32 columns; each block of 32
-// sequences is one 32x32 tile per wave (8 MFMAs over d), staged through LDS
+// query tokens is one 32x32 tile per wave (8 MFMAs over d), staged through LDS
 // and stored into qt in the attention kernel's fragment order:
-//   qt[b][head block hb][k-step st][lane][8], lane = 32 g + (h % 32),
-// holding the absorbed-query / q_pe elements 16 st + 8 g .. +7 of head
-// 32 hb + (h % 32), so that each of the attention's query loads reads 1 KB
-// contiguous per wave.  Padded heads are zero.
+//   qt[it][row block rb][k-step st][lane][8], lane = 32 g + (row % 32),
+// holding the absorbed-query / q_pe elements 16 st + 8 g .. +7 of row
+// 32 rb + (row % 32), so that each of the attention's query loads reads 1 KB
+// contiguous per wave.  Workgroup H + j zeroes padding row ps H + j of every
+// item.
 // ---------------------------------------------------------------------------
 template <int WRITE>
 __global__ __launch_bounds__(256, 3) void absorb_kernel(const uint16_t* __restrict__ q_nope,
                                                      const uint16_t* __restrict__ q_pe,
                                                      const uint16_t* __restrict__ wkv_b,
-                                                     uint16_t* __restrict__ qt, int B, int s, int H,
-                                                     int Hp, int bz, const int32_t* __restrict__ lens,
+                                                     uint16_t* __restrict__ qt, int B, int s, int ps,
+                                                     int H, int Hx, int Hp, int bz,
+                                                     const int32_t* __restrict__ lens,
                                                      int T, int topk, int min_group_tiles,
                                                      int G, int32_t* wcum, int4* rec,
                                                      int32_t* slot_of, RowWrite rw) {
@@ -333,27 +338,36 @@ __global__ __launch_bounds__(256, 3) void absorb_kernel(const uint16_t* __restri
   constexpr int kLds = 128 * kWRow * 2 > kPlanLdsBytes ? 128 * kWRow * 2 : kPlanLdsBytes;
   __shared__ __attribute__((aligned(16))) char smem[kLds];
   const int h = blockIdx.x, cblk = blockIdx.y, tid = threadIdx.x;
-  if (h >= Hp) {
+  const int NI = B / ps;  // work items
+  if (h >= Hx) {
     if (blockIdx.z != 0) return;
-    if (h == Hp) {
-      if (cblk == 0) plan_groups(lens, B, s, T, topk, min_group_tiles, G, wcum, rec, slot_of, smem);
+    if (h == Hx) {  // the plan is over work items, each seeing its last token's rows
+      if (cblk == 0) plan_groups(lens, NI, s / ps, T, topk, min_group_tiles, G, wcum, rec, slot_of, smem);
     } else if (WRITE != kNoWrite) {
-      write_new_rows<WRITE>(rw, lens, B, s, T, (h - Hp - 1) * 4 + cblk, (gridDim.x - Hp - 1) * 4);
+      write_new_rows<WRITE>(rw, lens, B, s, T, (h - Hx - 1) * 4 + cblk, (gridDim.x - Hx - 1) * 4);
     }
     return;
   }
   const int b_lo = blockIdx.z * bz, b_hi = min(B, b_lo + bz);
-  const int HB = Hp >> 5, hb = h >> 5, hn = h & 31;
-  // element offset of chunk (8 values from c, c % 8 == 0) of (b, h) in qt
-  auto frag = [&](int b, int c) -> size_t {
-    return (((size_t)b * HB + hb) * 36 + (c >> 4)) * 512 + (((c >> 3) & 1) * 32 + hn) * 8;
+  const int HB = Hp >> 5;
+  // element offset of chunk (8 values from c, c % 8 == 0) of query row `row`
+  // of work item it in qt
+  auto frag_row = [&](int it, int row, int c) -> size_t {
+    return (((size_t)it * HB + (row >> 5)) * 36 + (c >> 4)) * 512 + (((c >> 3) & 1) * 32 + (row & 31)) * 8;
   };
-  if (h >= H) {  // padding heads: zero rows (the attention waves read them)
+  // the same for head h of query token b
+  auto frag = [&](int b, int c) -> size_t {
+    const int it = ps == 1 ? b : b / ps;
+    return frag_row(it, (b - it * ps) * H + h, c);
+  };
+  if (h >= H) {  // padding rows: zero (the attention waves read them); items are
+                 // numbered below the tokens, so the z ranges cover them too
+    const int row = ps * H + (h - H), it_hi = min(b_hi, NI);
     const int per_b = cblk == 0 ? 24 : 16;
-    for (int i = tid; i < (b_hi - b_lo) * per_b; i += 256) {
-      const int b = b_lo + i / per_b, ch = i % per_b;
+    for (int i = tid; i < (it_hi - b_lo) * per_b; i += 256) {
+      const int it = b_lo + i / per_b, ch = i % per_b;
       const int c = ch < 16 ? cblk * 128 + 8 * ch : kC + 8 * (ch - 16);
-      *(u32x4*)(qt + frag(b, c)) = u32x4{0, 0, 0, 0};
+      *(u32x4*)(qt + frag_row(it, row, c)) = u32x4{0, 0, 0, 0};
     }
     return;
   }
@@ -477,9 +491,12 @@ struct AttnArgs {
   const int32_t* topk_idx;
   const int4* rec;        // [grid] {sequence or -1, first tile, end tile, length}
   const int32_t* slot_of; // [grid] plan slot (partial index) of each workgroup
-  uint16_t* part_o;       // [grid][H][512]
+  uint16_t* part_o;       // [grid][Hp][512]
   float* part_ml;         // [grid][H][2]
-  int B, s, H, Hp, T, topk, head_blocks;  // B: query tokens (batch x s)
+  // H: query rows per work item (ps x heads), Hp: H padded to 32; s: work
+  // items per sequence (item b reads sequence b / s); ps: query tokens per
+  // item (1, or the sequence's s tokens, rows i hq .. for token i); hq: heads
+  int s, H, Hp, T, topk, head_blocks, ps, hq;
   int head_split;  // workgroups per plan workgroup, each with head_blocks / head_split blocks
   float scale_log2;
 };
@@ -550,8 +567,10 @@ struct Stage {
 
 // NHB: head blocks per workgroup the update keeps accumulators for (4; or the
 // workgroup's exact count 1 or 2 when it has that few: no MFMAs on blocks
-// whose probabilities would all be zero).
-template <bool FP8, bool TOPK, int NHB>
+// whose probabilities would all be zero).  PACK: the work item is a sequence
+// whose ps query tokens share the tiles; each query row is then masked at its
+// own token's length (token i of ps sees len - (ps - 1 - i) rows).
+template <bool FP8, bool TOPK, int NHB, bool PACK = false>
 __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   // Workgroup x runs head group hq (of HS) of plan workgroup grp; the HS
   // workgroups of one plan workgroup sit on its XCD (x % 8 == grp % 8) and
@@ -568,7 +587,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   const int n_b = TOPK ? (len > 0 ? a.topk : 0) : len;
   const int p0 = t_lo * kTT, p1 = min(t_hi * kTT, n_b);
   const int ntiles = t_hi - t_lo;
-  const size_t seq_row0 = (size_t)(a.s == 1 ? b : b / a.s) * a.T;  // b: query token
+  const size_t seq_row0 = (size_t)(a.s == 1 ? b : b / a.s) * a.T;  // b: work item
   const size_t slot_id = part_slot;
 
   // One LDS array per ring slot (not one 2-D array): the slot a tile lives in
@@ -595,7 +614,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   const bool active = wave < nhb;  // this wave has score heads
   const int n = lane & 31, g = lane >> 5;
   const int head = wave * 32 + n;           // in this workgroup (P rows, alpha)
-  const int ghead = (hb0 + wave) * 32 + n;  // in the layer
+  const int ghead = (hb0 + wave) * 32 + n;  // query row of the work item
+  // rows this lane's query token sees (padding rows: any value)
+  const int row_lim = PACK ? len - (a.ps - 1 - min(ghead / a.hq, a.ps - 1)) : len;
 
   // P rows and l of heads without a score wave stay zero; their alpha stays 1.
   for (int i = tid; i < 2 * 128 * kPStride / 2; i += kAttnThreads) ((uint32_t*)sP)[i] = 0u;
@@ -1225,7 +1246,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     } else if (gather) {
       dma_all(gc, p0 + (j + 1) * kTT, gbase);
     }
-    const uint32_t mask = sMask[st];
+    uint32_t mask = sMask[st];
+    if constexpr (PACK) {  // and the rows this lane's token sees (per lane)
+      const int r = row_lim - (p0 + j * kTT);
+      mask = r >= kTT ? mask : (r <= 0 ? 0u : mask & ((1u << r) - 1u));
+    }
     // one code path for every wave inside the loop (branches around the
     // update would merge 256 accumulator registers); the first tile, which
     // has no update before it, is peeled off the loop
@@ -1283,13 +1308,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// combine: grid (B, head_blocks * 32 partial rows), 64 x NG threads (NG =
-// 1, 2, 4 or 8 groups, about one per four partials a sequence has on
-// average).  Row r of a partial is (head block r / 32, wave, m, q2) in the
-// attention kernel's fragment order: 64 lanes x 8 values, lane l holding head
-// 32 (r / 32) + l % 32.  Thread (lane, group sg) merges that chunk over every
-// NG-th partial of sequence b (slots wcum[b] .. wcum[b+1] - 1) with a running
-// maximum, the groups are merged through LDS, and
+// combine: grid (work items, head_blocks * 32 partial rows), 64 x NG threads
+// (NG = 1, 2, 4 or 8 groups, about one per four partials an item has on
+// average).  H here counts an item's query rows.  Row r of a partial is (row
+// block r / 32, wave, m, q2) in the attention kernel's fragment order: 64
+// lanes x 8 values, lane l holding query row 32 (r / 32) + l % 32.  Thread
+// (lane, group sg) merges that chunk over every NG-th partial of item b
+// (slots wcum[b] .. wcum[b+1] - 1) with a running maximum, the groups are
+// merged through LDS, and
 //   o = sum_j 2^(m_j - M) O_j / sum_j 2^(m_j - M) l_j,  M = max_j m_j
 // (over the partials with l_j > 0; none: zeros) goes to olat[b][h][c].
 // ---------------------------------------------------------------------------
@@ -1445,6 +1471,7 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
                          hipStream_t stream, void* latent_out) {
   const DecodePlan plan = make_decode_plan(p);
   const int s = p.seqlen_q, B = p.batch * s, H = p.num_heads;  // B: query tokens
+  const int ps = plan.pack_s, NI = (int)plan.items, rows = plan.rows;  // work items of ps tokens
   char* ws = (char*)d.workspace;
   uint16_t* qt = (uint16_t*)(ws + plan.off_qt);
   uint16_t* part_o = (uint16_t*)(ws + plan.off_part_o);
@@ -1472,9 +1499,11 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
   // sequences per absorb workgroup: blocks of 32, over at most 8 ranges
   const int chunks = (B + 31) / 32, zs = std::min(chunks, 8);
   const int bz = 32 * ((chunks + zs - 1) / zs);
-  err = launch_kernel(absorb, dim3(plan.heads_padded + 1 + write_cols, 4, (B + bz - 1) / bz),
+  // columns: H heads, the padding rows of an item, the planner, the writers
+  const int hx = H + (plan.heads_padded - rows);
+  err = launch_kernel(absorb, dim3(hx + 1 + write_cols, 4, (B + bz - 1) / bz),
                       dim3(256), stream, evk(0), (const uint16_t*)d.q_nope, (const uint16_t*)d.q_pe,
-                      (const uint16_t*)d.wkv_b, qt, B, s, H, plan.heads_padded, bz, d.cache_lens,
+                      (const uint16_t*)d.wkv_b, qt, B, s, ps, H, hx, plan.heads_padded, bz, d.cache_lens,
                       p.max_seq_len, p.topk, plan.min_group_tiles, (int)plan.max_groups, wcum, rec,
                       slot_of, rw);
   if (err != hipSuccess) return err;
@@ -1489,10 +1518,11 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
   aa.slot_of = slot_of;
   aa.part_o = part_o;
   aa.part_ml = part_ml;
-  aa.B = B;
-  aa.s = s;
-  aa.H = H;
+  aa.s = s / ps;
+  aa.H = rows;
   aa.Hp = plan.heads_padded;
+  aa.ps = ps;
+  aa.hq = H;
   aa.T = p.max_seq_len;
   aa.topk = p.topk;
   aa.head_blocks = plan.head_blocks;
@@ -1504,16 +1534,20 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
   auto attn = fp8 ? (topk ? attn_kernel<true, true, 4> : attn_kernel<true, false, 4>)
                   : (topk ? (nhb == 1 ? attn_kernel<false, true, 1> : nhb == 2 ? attn_kernel<false, true, 2> : attn_kernel<false, true, 4>)
                           : (nhb == 1 ? attn_kernel<false, false, 1> : nhb == 2 ? attn_kernel<false, false, 2> : attn_kernel<false, false, 4>));
+  if (ps > 1)  // packed tokens (dense selections only)
+    attn = fp8 ? attn_kernel<true, false, 4, true>
+               : (nhb == 1 ? attn_kernel<false, false, 1, true> : nhb == 2 ? attn_kernel<false, false, 2, true> : attn_kernel<false, false, 4, true>);
   err = launch_kernel(attn, agrid, dim3(kAttnThreads), stream, evk(1), aa);
   if (err != hipSuccess) return err;
 
   // partial groups per combine thread block: about one per 4 partials of the
   // average sequence (at most 256 partials are in use when B <= 256)
-  const long long avg_parts = std::max<long long>(1, std::min<long long>(plan.max_groups, 256) / B);
+  // (work items: olat [item][ps H rows][512] is olat [token][H][512])
+  const long long avg_parts = std::max<long long>(1, std::min<long long>(plan.max_groups, 256) / NI);
   const int ng = avg_parts >= 32 ? 8 : (avg_parts >= 16 ? 4 : (avg_parts >= 8 ? 2 : 1));
-  err = launch_kernel_lds(combine_kernel, dim3(B, plan.head_blocks * 32), dim3(64 * ng),
+  err = launch_kernel_lds(combine_kernel, dim3(NI, plan.head_blocks * 32), dim3(64 * ng),
                           (size_t)(ng - 1) * 64 * 10 * sizeof(float), stream, evk(2),
-                      (const uint16_t*)part_o, (const float*)part_ml, (const int32_t*)wcum, olat, H,
+                      (const uint16_t*)part_o, (const float*)part_ml, (const int32_t*)wcum, olat, rows,
                       plan.heads_padded);
   if (err != hipSuccess) return err;
   if (latent_out) return hipSuccess;  // the caller takes the latent output

@@ -28,7 +28,16 @@ constexpr int kMaxTopkGroupTiles = 32;  // top-k: tiles per workgroup (index sta
 // The lengths live on the device, so w_b and S are computed there; the sizes
 // here are upper bounds.
 struct DecodePlan {
-  int heads_padded;     // H rounded up to a multiple of 32 (one 32-head block per wave)
+  // Work items.  Normally each query token (batch x seqlen_q of them) is an item
+  // with H query rows.  With s > 1 query tokens, a dense selection and s x H <=
+  // 128, the s tokens of a sequence share one item instead: its rows are the
+  // packed (token i, head h) pairs, row i H + h, so every tile of the sequence
+  // is read and scored once for all of them (each row masked at its token's
+  // own limit).
+  long long items;      // work items: batch (packed) or batch x seqlen_q
+  int pack_s;           // tokens per item: seqlen_q when packed, else 1
+  int rows;             // query rows per item: pack_s x H
+  int heads_padded;     // rows rounded up to a multiple of 32 (one 32-row block per wave)
   int head_blocks;      // heads_padded / 32
   int head_split;       // attention workgroups per plan workgroup (1, 2 or 4), each
                         // with head_blocks / head_split of the head blocks
@@ -47,9 +56,14 @@ inline DecodePlan make_decode_plan(const mla_params& p) {
   // its own over the rows it sees)
   // (64-bit: the product is formed before the caller's limit on it is known
   // to hold; mla_decode rejects batch x seqlen_q > 65535)
-  const long long B = (long long)p.batch * (p.seqlen_q > 0 ? p.seqlen_q : 1);
+  const int sq = p.seqlen_q > 0 ? p.seqlen_q : 1;
   const int H = p.num_heads;
-  d.heads_padded = (H + 31) / 32 * 32;
+  const bool pack = sq > 1 && p.topk == 0 && (long long)sq * H <= 128;
+  d.pack_s = pack ? sq : 1;
+  d.items = pack ? (long long)p.batch : (long long)p.batch * sq;
+  d.rows = d.pack_s * H;
+  const long long B = d.items;
+  d.heads_padded = (d.rows + 31) / 32 * 32;
   d.head_blocks = d.heads_padded / 32;
   const long long n_max = p.topk > 0 ? p.topk : p.max_seq_len;
   d.max_tiles = (n_max + kTileRows - 1) / kTileRows;
@@ -73,15 +87,15 @@ inline DecodePlan make_decode_plan(const mla_params& p) {
          G * 2 * d.head_split <= kTargetCUs)
     d.head_split *= 2;
   size_t off = 0;
-  d.off_qt = off;  // bf16 [B tokens][heads_padded][576], in the attention kernel's fragment order
+  d.off_qt = off;  // bf16 [items][heads_padded][576], in the attention kernel's fragment order
   off = align256(off + (size_t)B * d.heads_padded * 576 * 2);
   d.off_part_o = off;  // bf16 [max_groups][heads_padded][512], in fragment order
   off = align256(off + (size_t)G * d.heads_padded * 512 * 2);
-  d.off_part_ml = off;  // fp32 [max_groups][H][2]
-  off = align256(off + (size_t)G * H * 2 * 4);
-  d.off_olat = off;  // bf16 [B][H][512]
-  off = align256(off + (size_t)B * H * 512 * 2);
-  d.off_wcum = off;  // int32 [B + 1]: w_b, w_B = workgroups in use
+  d.off_part_ml = off;  // fp32 [max_groups][rows][2]
+  off = align256(off + (size_t)G * d.rows * 2 * 4);
+  d.off_olat = off;  // bf16 [items][rows][512] = [batch x seqlen_q tokens][H][512]
+  off = align256(off + (size_t)B * d.rows * 512 * 2);
+  d.off_wcum = off;  // int32 [items + 1]: w_b, w_B = workgroups in use
   off = align256(off + ((size_t)B + 1) * 4);
   d.off_rec = off;  // int32 [max_groups][4]: sequence (-1: unused), first tile, end tile, length
   off = align256(off + (size_t)G * 16);

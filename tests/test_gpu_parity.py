@@ -469,6 +469,39 @@ def test_multitoken_decode(m, B, s, H, T, fp8, topk):
         assert (out[2, 0].float() == 0).all()
 
 
+# A sequence's s tokens share one attention work item when the selection is
+# dense and s x H <= 128: query rows are packed as token i, head h -> row
+# i H + h, and each row is masked at its own token's length.  Cases: one, two
+# and four row blocks, padding rows (48 and 100 of a 64- or 128-row block, a
+# head count that is not a multiple of 16), the FP8 cache, lengths at and
+# around the token count and the 32-row tile boundaries, a sequence of many
+# tiles split over several workgroups, and the latent output of the same path.
+@pytest.mark.parametrize("B,s,H,T,fp8", [(6, 2, 16, 700, False), (6, 3, 16, 300, False),
+                                         (5, 8, 16, 1200, False), (6, 5, 20, 450, False),
+                                         (4, 2, 64, 2000, True), (6, 4, 32, 333, True)])
+def test_packed_tokens(m, B, s, H, T, fp8):
+    x = multitoken_case(B, s, H, T, fp8, 0, seed=13 * s + H + T)
+    lens = x["cache_lens"]
+    edge = [T, 0, s - 1, s, 32 + s - 1, 65]
+    for i in range(min(B, len(edge))):
+        lens[i] = min(edge[i], T)
+    kv, sc, pe = host_caches(x, T, fp8)
+    print(f"[packed] B={B} s={s} H={H} T={T} fp8={fp8} lens={lens.tolist()}", flush=True)
+    args = (to_dev(x["q_nope"]), to_dev(x["q_pe"]), to_dev(x["wkv_b"]), to_dev(kv), to_dev(pe),
+            to_dev(lens))
+    out = m.decode(*args, kv_scale=to_dev(sc))
+    lat = m.decode_latent(*args, kv_scale=to_dev(sc))
+    torch.cuda.synchronize()
+    oargs = (x["q_nope"], x["q_pe"], x["wkv_b"], kv, pe, lens, synth.SOFTMAX_SCALE)
+    osc = None if sc is None else sc.numpy()
+    ref = oracle.decode(*oargs, kv_scale=osc)
+    check(out, ref, fp8, f"packed B{B} s{s} H{H} fp8={fp8}")
+    check(lat, oracle.decode_latent(*oargs, kv_scale=osc), fp8, f"packed latent B{B} s{s} H{H}")
+    assert (out[1].float() == 0).all()      # length 0: no token sees a row
+    assert (out[2, 0].float() == 0).all()   # length s - 1: the first token sees none
+    assert not (out[2, 1:].float() == 0).all()
+
+
 def _sweep_configs(n=20, seed=2026):
     """Deterministic draw of small shapes over every plan path: batch, query
     tokens, head count (whole, padded and odd head blocks, so the head split
