@@ -615,8 +615,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
   const int n = lane & 31, g = lane >> 5;
   const int head = wave * 32 + n;           // in this workgroup (P rows, alpha)
   const int ghead = (hb0 + wave) * 32 + n;  // query row of the work item
-  // rows this lane's query token sees (padding rows: any value)
-  const int row_lim = PACK ? len - (a.ps - 1 - min(ghead / a.hq, a.ps - 1)) : len;
+  // Rows this lane's query token sees (padding rows: any value), recomputed
+  // from the lane number at each use: a value held across the loop would take
+  // a register the score chain needs.
+  auto row_lim = [&]() MLA_INLINE -> int {
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+    const int row = (hb0 + wave) * 32 + (ln & 31);
+    return len - (a.ps - 1 - min(row / a.hq, a.ps - 1));
+  };
 
   // P rows and l of heads without a score wave stay zero; their alpha stays 1.
   for (int i = tid; i < 2 * 128 * kPStride / 2; i += kAttnThreads) ((uint32_t*)sP)[i] = 0u;
@@ -1248,7 +1255,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void attn_kernel(AttnArgs a) {
     }
     uint32_t mask = sMask[st];
     if constexpr (PACK) {  // and the rows this lane's token sees (per lane)
-      const int r = row_lim - (p0 + j * kTT);
+      const int r = row_lim() - (p0 + j * kTT);
       mask = r >= kTT ? mask : (r <= 0 ? 0u : mask & ((1u << r) - 1u));
     }
     // one code path for every wave inside the loop (branches around the
@@ -1466,6 +1473,12 @@ __global__ __launch_bounds__(64) void uproj_kernel(const uint16_t* __restrict__ 
   }
 }
 
+// The attention instance for a workgroup's head-block count (1, 2, or up to 4).
+template <bool FP8, bool TOPK, bool PACK>
+static void (*attn_instance(int nhb))(AttnArgs) {
+  return nhb == 1 ? attn_kernel<FP8, TOPK, 1, PACK> : nhb == 2 ? attn_kernel<FP8, TOPK, 2, PACK> : attn_kernel<FP8, TOPK, 4, PACK>;
+}
+
 // ---------------------------------------------------------------------------
 hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWriteArgs* write,
                          hipStream_t stream, void* latent_out) {
@@ -1529,14 +1542,13 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
   aa.head_split = plan.head_split;
   aa.scale_log2 = p.softmax_scale * 1.4426950408889634f;
   const dim3 agrid((unsigned)(plan.max_groups * plan.head_split));
-  // bf16 workgroups with one or two head blocks get their own accumulator count
+  // workgroups with one or two head blocks get their own accumulator count
   const int nhb = plan.head_blocks / plan.head_split;
-  auto attn = fp8 ? (topk ? attn_kernel<true, true, 4> : attn_kernel<true, false, 4>)
-                  : (topk ? (nhb == 1 ? attn_kernel<false, true, 1> : nhb == 2 ? attn_kernel<false, true, 2> : attn_kernel<false, true, 4>)
-                          : (nhb == 1 ? attn_kernel<false, false, 1> : nhb == 2 ? attn_kernel<false, false, 2> : attn_kernel<false, false, 4>));
-  if (ps > 1)  // packed tokens (dense selections only)
-    attn = fp8 ? attn_kernel<true, false, 4, true>
-               : (nhb == 1 ? attn_kernel<false, false, 1, true> : nhb == 2 ? attn_kernel<false, false, 2, true> : attn_kernel<false, false, 4, true>);
+  // (packed tokens: dense selections only)
+  auto attn = fp8 ? (topk ? attn_instance<true, true, false>(nhb)
+                          : ps > 1 ? attn_instance<true, false, true>(nhb) : attn_instance<true, false, false>(nhb))
+                  : (topk ? attn_instance<false, true, false>(nhb)
+                          : ps > 1 ? attn_instance<false, false, true>(nhb) : attn_instance<false, false, false>(nhb));
   err = launch_kernel(attn, agrid, dim3(kAttnThreads), stream, evk(1), aa);
   if (err != hipSuccess) return err;
 

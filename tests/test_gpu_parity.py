@@ -478,7 +478,8 @@ def test_multitoken_decode(m, B, s, H, T, fp8, topk):
 # tiles split over several workgroups, and the latent output of the same path.
 @pytest.mark.parametrize("B,s,H,T,fp8", [(6, 2, 16, 700, False), (6, 3, 16, 300, False),
                                          (5, 8, 16, 1200, False), (6, 5, 20, 450, False),
-                                         (4, 2, 64, 2000, True), (6, 4, 32, 333, True)])
+                                         (4, 2, 64, 2000, True), (6, 4, 32, 333, True),
+                                         (6, 7, 1, 260, False), (6, 40, 3, 500, True)])
 def test_packed_tokens(m, B, s, H, T, fp8):
     x = multitoken_case(B, s, H, T, fp8, 0, seed=13 * s + H + T)
     lens = x["cache_lens"]
