@@ -73,7 +73,10 @@ typedef enum mla_kv_dtype {
  *                 query tokens per sequence for mla_decode / mla_decode_step
  *                 (>= 1, batch * s <= 65535): the s tokens are the last s
  *                 cached positions of the sequence, and token i (0-based)
- *                 sees the rows up to its own, t < end_b - (s - 1 - i)
+ *                 sees the rows up to its own, t < end_b - (s - 1 - i).
+ *                 With a dense selection and s * num_heads <= 128 the s
+ *                 tokens share the reads and the score work of each cache
+ *                 tile
  *   num_heads     H, 1..128 (the local heads of this GPU)
  *   max_seq_len   T: second dimension of every cache buffer, >= 1
  *   kv_lora_rank, qk_nope_dim, qk_rope_dim, v_head_dim: must be 512, 128, 64, 128
