@@ -474,8 +474,9 @@ def test_multitoken_decode(m, B, s, H, T, fp8, topk):
 # i H + h, and each row is masked at its own token's length.  Cases: one, two
 # and four row blocks, padding rows (48 and 100 of a 64- or 128-row block, a
 # head count that is not a multiple of 16), the FP8 cache, lengths at and
-# around the token count and the 32-row tile boundaries, a sequence of many
-# tiles split over several workgroups, and the latent output of the same path.
+# around the token count and the 32-row tile boundaries, a length past the
+# buffer, a sequence of many tiles split over several workgroups, and the
+# latent output of the same path.
 @pytest.mark.parametrize("B,s,H,T,fp8", [(6, 2, 16, 700, False), (6, 3, 16, 300, False),
                                          (5, 8, 16, 1200, False), (6, 5, 20, 450, False),
                                          (4, 2, 64, 2000, True), (6, 4, 32, 333, True),
@@ -483,9 +484,9 @@ def test_multitoken_decode(m, B, s, H, T, fp8, topk):
 def test_packed_tokens(m, B, s, H, T, fp8):
     x = multitoken_case(B, s, H, T, fp8, 0, seed=13 * s + H + T)
     lens = x["cache_lens"]
-    edge = [T, 0, s - 1, s, 32 + s - 1, 65]
+    edge = [T, 0, s - 1, s, 32 + s - 1, T + 3]  # (a length past T is clamped to T)
     for i in range(min(B, len(edge))):
-        lens[i] = min(edge[i], T)
+        lens[i] = edge[i] if i == 5 else min(edge[i], T)
     kv, sc, pe = host_caches(x, T, fp8)
     print(f"[packed] B={B} s={s} H={H} T={T} fp8={fp8} lens={lens.tolist()}", flush=True)
     args = (to_dev(x["q_nope"]), to_dev(x["q_pe"]), to_dev(x["wkv_b"]), to_dev(kv), to_dev(pe),
