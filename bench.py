@@ -43,7 +43,9 @@ PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20
 METRIC = "MLA decode tokens/s + latent-cache HBM GB/s (% of peak), H=128, T=4K–64K"
 HEADLINE = "ragged_b32_h128_t16384"
-EXTRA = ["dense_b1_h128_t4096", "fp8_b16_h128_t32768", "topk2048_b8_h128_t65536"]
+EXTRA = ["dense_b1_h128_t4096", "fp8_b16_h128_t32768", "topk2048_b8_h128_t65536",
+         # one GPU's 16 of 128 heads with two query tokens per sequence (shared tile work)
+         "ragged_b32_h128_t16384:16:2"]
 KERNELS = ["absorb", "attention", "combine", "uproj"]
 FUSED = True  # --unfused: the row store runs as its own mla_cache_write kernel
 
@@ -505,7 +507,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--extra", default=",".join(EXTRA),
-                    help="comma-separated workloads timed after the headline one ('' for none)")
+                    help="comma-separated workloads timed after the headline one ('' for none); "
+                         "name:H:s runs a workload with H heads and s query tokens per sequence")
     ap.add_argument("--extra-steps", type=int, default=300)
     ap.add_argument("--extra-warmup", type=int, default=100)
     ap.add_argument("--replicas", type=int, default=0, help="0: enough to exceed the MALL")
@@ -561,13 +564,19 @@ def main():
           flush=True)
     head, x = measure(w, args, args.steps, args.warmup, mla, synth, torch, np, S)
     configs = {}
-    for name in [n for n in args.extra.split(",") if n and n != args.workload]:
-        we = synth.WORKLOADS[name]
-        print(f"bench: {name} s={S}: {args.extra_warmup} warmup + {args.extra_steps} timed steps",
+    for spec in [n for n in args.extra.split(",") if n and n != args.workload]:
+        name, *over = spec.split(":")
+        we, Se = synth.WORKLOADS[name], S
+        if over:
+            heads, Se = int(over[0]), int(over[1]) if len(over) > 1 else S
+            if heads != we.heads:
+                we = synth.scaled(we, heads=heads, name=f"{we.name}_h{heads}")
+        print(f"bench: {we.name} s={Se}: {args.extra_warmup} warmup + {args.extra_steps} timed steps",
               file=sys.stderr, flush=True)
-        r, _ = measure(we, args, args.extra_steps, args.extra_warmup, mla, synth, torch, np, S)
+        r, _ = measure(we, args, args.extra_steps, args.extra_warmup, mla, synth, torch, np, Se)
         configs[r["config"]["workload"]] = {
             "tokens_per_s": r["value"], "ms_per_step": r["ms_per_step"], "steps": r["steps"],
+            "heads": r["config"]["heads"], "query_tokens": r["config"]["query_tokens"],
             "dtype": r["dtype"], "kv_cache": r["config"]["kv_cache"],
             "selection": r["config"]["selection"], "rows_per_step": r["config"]["rows_per_step"],
             "latent_cache_gbps": r["latent_cache_gbps"], "step_hbm_frac": r["step_hbm_frac"],
