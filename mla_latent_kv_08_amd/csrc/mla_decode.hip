@@ -113,13 +113,16 @@ __device__ __forceinline__ int xcd_workgroup(int s, int n) {
 }
 
 // Work plan of one decode call, computed by one workgroup of 256 threads (the
-// split is described with make_decode_plan) over the B query tokens (B = batch
-// x tokens per sequence, token v = b s + i seeing query_len rows of sequence
-// v / s): picks the tile budget S, then
+// split is described with make_decode_plan) over the B work items (item v =
+// b s + i seeing query_len rows of sequence v / s: the query tokens, s per
+// sequence, or with packed tokens the sequences, s = 1): picks the tile
+// budget S, then
 // writes wcum[b] = k_0 + ... + k_{b-1} (wcum[B] = workgroups in use) and, for
-// each of the G attention workgroups, the record {sequence, first tile, end
-// tile, clamped length} (sequence -1: workgroup unused) and the plan slot its
-// partial goes to, so that a workgroup starts from two independent loads.
+// each of the G attention workgroups, the record {item, first tile, end
+// tile, clamped length} (item -1: workgroup unused) and the plan slot its
+// partial goes to, so that a workgroup starts from two independent loads
+// (plan_groups, after two helpers).
+
 // floor(a / b) and ceil(a / b) for 0 <= a < 2^52 and b >= 1.  Both are
 // exact in double, and a non-integer quotient a/b lies at least 1/b from the
 // nearest integer n, more than half an ulp of n (n * 2^-53 < 1/b because
@@ -489,7 +492,7 @@ struct AttnArgs {
   const float* kv_scale;
   const uint16_t* pe;
   const int32_t* topk_idx;
-  const int4* rec;        // [grid] {sequence or -1, first tile, end tile, length}
+  const int4* rec;        // [grid] {work item or -1, first tile, end tile, length}
   const int32_t* slot_of; // [grid] plan slot (partial index) of each workgroup
   uint16_t* part_o;       // [grid][Hp][512]
   float* part_ml;         // [grid][H][2]

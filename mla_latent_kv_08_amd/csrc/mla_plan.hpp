@@ -16,8 +16,8 @@ constexpr int kTargetCUs = 256;
 constexpr int kTileRows = 32;           // cache rows per LDS tile of the attention kernel
 constexpr int kMaxTopkGroupTiles = 32;  // top-k: tiles per workgroup (index staging bound)
 
-// Work split of the attention kernel.  Sequence b has t_b tiles of 32
-// selected entries.  For a tile budget S, sequence b gets k_b = ceil(t_b / S)
+// Work split of the attention kernel.  Work item b has t_b tiles of 32
+// selected entries.  For a tile budget S, item b gets k_b = ceil(t_b / S)
 // workgroups, and workgroup i = w_b + p (w_b = k_0 + ... + k_{b-1}) takes its
 // tiles [floor(p t_b / k_b), floor((p+1) t_b / k_b)) and writes its partial
 // (O, m, l) into slot i.  S is the smallest budget with sum k_b <= 256 (one
@@ -52,8 +52,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 inline DecodePlan make_decode_plan(const mla_params& p) {
   DecodePlan d{};
-  // B: query tokens, batch x seqlen_q (each token is planned as a sequence of
-  // its own over the rows it sees)
+  // B: work items (each planned as a sequence of its own over the rows its
+  // last token sees), batch x seqlen_q or, with packed tokens, batch
   // (64-bit: the product is formed before the caller's limit on it is known
   // to hold; mla_decode rejects batch x seqlen_q > 65535)
   const int sq = p.seqlen_q > 0 ? p.seqlen_q : 1;
