@@ -17,9 +17,11 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _case(m, w, label):
+def _case(m, w, label, s=1):
     x = synth.make_inputs(w)
-    print(f"[noalloc {label}] B={w.batch} H={w.heads} T={w.max_seq_len} fp8={w.fp8} topk={w.topk}",
+    if s > 1:
+        x = synth.add_query_tokens(x, s, seed=w.seed + 1000)
+    print(f"[noalloc {label}] B={w.batch} s={s} H={w.heads} T={w.max_seq_len} fp8={w.fp8} topk={w.topk}",
           flush=True)
     d = {k: (None if v is None else v.to(DEV).contiguous()) for k, v in x.items()}
     kv, sc, pe = d["kv"], None, d["pe"]
@@ -63,6 +65,14 @@ def test_noalloc_fp8_topk_then_smaller_dense():
     _case(m, synth.Workload("na3", 4, 128, 2500, fp8=True, topk=600, outlier_frac=0.01,
                             outlier_mult=20.0, seed=93), "fp8 top-k")
     _case(m, synth.Workload("na4", 1, 16, 256, seed=94), "tiny dense")
+
+
+def test_noalloc_packed_tokens_then_smaller():
+    """Several query tokens per sequence at few heads (the tokens share one
+    work item: s H packed query rows), then a smaller call of the same kind."""
+    from mla_latent_kv_08_amd import mla as m
+    _case(m, synth.Workload("na5", 5, 16, 900, ragged=(4, 900), seed=95), "packed H=16 s=4", s=4)
+    _case(m, synth.Workload("na6", 2, 32, 300, ragged=(3, 300), seed=96), "packed H=32 s=3, smaller", s=3)
 
 
 def test_noalloc_in_a_captured_graph():
