@@ -169,6 +169,21 @@ def kernel_symbol(name, w):
             "uproj": "mla::uproj_kernel"}[name]
 
 
+def extra_workload(spec, synth, s_default):
+    """An --extra entry: a workload name, or name:H:s for that workload with H
+    heads and s query tokens per sequence (renamed <name>_h<H>).  Returns the
+    workload and its s."""
+    name, *over = spec.split(":")
+    w, s = synth.WORKLOADS[name], s_default
+    if over:
+        heads = int(over[0])
+        if len(over) > 1:
+            s = int(over[1])
+        if heads != w.heads:
+            w = synth.scaled(w, heads=heads, name=f"{w.name}_h{heads}")
+    return w, s
+
+
 def workload_bytes_flops(w, lens, k, s=1):
     """Algorithmic bytes and FLOPs per kernel launch (one step).  With s query
     tokens per sequence the cache rows count once per sequence (the method
@@ -565,12 +580,7 @@ def main():
     head, x = measure(w, args, args.steps, args.warmup, mla, synth, torch, np, S)
     configs = {}
     for spec in [n for n in args.extra.split(",") if n and n != args.workload]:
-        name, *over = spec.split(":")
-        we, Se = synth.WORKLOADS[name], S
-        if over:
-            heads, Se = int(over[0]), int(over[1]) if len(over) > 1 else S
-            if heads != we.heads:
-                we = synth.scaled(we, heads=heads, name=f"{we.name}_h{heads}")
+        we, Se = extra_workload(spec, synth, S)
         print(f"bench: {we.name} s={Se}: {args.extra_warmup} warmup + {args.extra_steps} timed steps",
               file=sys.stderr, flush=True)
         r, _ = measure(we, args, args.extra_steps, args.extra_warmup, mla, synth, torch, np, Se)

@@ -71,3 +71,17 @@ def test_per_kernel_bytes_add_up():
         assert sum(f for _, f in out.values()) == total_flops, name
         stores = w.batch * 2 * 576 + w.batch * row_bytes + 4 * w.batch if bench.FUSED else 0
         assert sum(b for b, _ in out.values()) - stores == total_bytes, name
+
+
+def test_extra_workload_specs():
+    w, s = bench.extra_workload("dense_b1_h128_t4096", synth, 1)
+    assert (w.name, w.heads, s) == ("dense_b1_h128_t4096", 128, 1)
+    w, s = bench.extra_workload("ragged_b32_h128_t16384:16:2", synth, 1)
+    assert (w.name, w.heads, w.batch, s) == ("ragged_b32_h128_t16384_h16", 16, 32, 2)
+    w, s = bench.extra_workload("fp8_b16_h128_t32768:32", synth, 3)
+    assert (w.name, w.heads, w.fp8, s) == ("fp8_b16_h128_t32768_h32", 32, True, 3)
+    # the default run's packed line has its counter rows in the committed summary
+    for kernel in ["absorb", "attention", "combine", "uproj"]:
+        w, s = bench.extra_workload(bench.EXTRA[-1], synth, 1)
+        assert bench.counter_traffic(f"{w.name}_s{s}", bench.kernel_symbol(kernel, w),
+                                     check_sources=False), kernel
