@@ -504,6 +504,27 @@ def test_packed_tokens(m, B, s, H, T, fp8):
     assert not (out[2, 1:].float() == 0).all()
 
 
+def test_packed_tokens_full_size_sampled(m):
+    """The benchmark's packed configuration at full size, with its inputs (the
+    same seeds): ragged B=32 over a 16384-row buffer at 16 heads with two query
+    tokens per sequence (one work item of 32 packed rows per sequence); both
+    tokens of every sequence are checked, at two heads each, plus the corners."""
+    w = synth.scaled(synth.WORKLOADS["ragged_b32_h128_t16384"], heads=16, name="ragged_b32_h128_t16384_h16")
+    s = 2
+    x = synth.add_query_tokens(synth.make_inputs(w), s, seed=w.seed + 1000)
+    print(f"[packed full] B={w.batch} s={s} H={w.heads} T={w.max_seq_len}", flush=True)
+    out = m.decode(to_dev(x["q_nope"]), to_dev(x["q_pe"]), to_dev(x["wkv_b"]), to_dev(x["kv"]),
+                   to_dev(x["pe"]), to_dev(x["cache_lens"]))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(77)
+    pairs = [(q, int(h)) for q in range(w.batch * s) for h in rng.choice(w.heads, 2, replace=False)]
+    pairs += [(0, 0), (w.batch * s - 1, w.heads - 1)]
+    ref = oracle.decode(x["q_nope"], x["q_pe"], x["wkv_b"], x["kv"], x["pe"], x["cache_lens"],
+                        synth.SOFTMAX_SCALE, pairs=pairs)
+    got = out.reshape(w.batch * s, w.heads, 128)[[p[0] for p in pairs], [p[1] for p in pairs]]
+    check(got, ref, False, "packed full-size sampled")
+
+
 def _sweep_configs(n=20, seed=2026):
     """Deterministic draw of small shapes over every plan path: batch, query
     tokens, head count (whole, padded and odd head blocks, so the head split
