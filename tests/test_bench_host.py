@@ -85,3 +85,14 @@ def test_extra_workload_specs():
         w, s = bench.extra_workload(bench.EXTRA[-1], synth, 1)
         assert bench.counter_traffic(f"{w.name}_s{s}", bench.kernel_symbol(kernel, w),
                                      check_sources=False), kernel
+
+
+def test_more_than_one_gpu_is_refused():
+    """The benchmark measures one GPU; asking for more exits with a message
+    (before touching torch or a device)."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2, r
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
