@@ -1424,10 +1424,11 @@ __global__ __launch_bounds__(64 * kCombineGroups) void combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// uproj: out[b,h,d] = sum_c o[b,h,c] W_UV[h][d][c].  grid (H, 4 d-blocks of 32),
-// one wave; MFMA 16x16x32 with the sequences as the M dimension (blocks of 16)
-// and two 16-wide d blocks as N.  The wave's W_UV slice (32 rows x 512, 32 KB)
-// is loaded into registers up front and reused for every block of sequences.
+// uproj: out[b,h,d] = sum_c o[b,h,c] W_UV[h][d][c].  grid (H, 4 d-blocks of 32,
+// shares of the query tokens), one wave; MFMA 16x16x32 with the tokens as the
+// M dimension (blocks of 16) and two 16-wide d blocks as N.  The wave's W_UV
+// slice (32 rows x 512, 32 KB) is loaded into registers up front and reused
+// for every block of tokens of its share.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void uproj_kernel(const uint16_t* __restrict__ olat,
                                                    const uint16_t* __restrict__ wkv_b,
@@ -1445,7 +1446,11 @@ __global__ __launch_bounds__(64) void uproj_kernel(const uint16_t* __restrict__ 
   // the first block's rows go out with the weights, and each next block's
   // before the current block's MFMAs, so only one load latency is exposed
   u32x4 av[16], an[16];
-  load_a(0, av);
+  // this workgroup's token blocks: a contiguous share of the ceil(B / 16)
+  const int nblk = (B + 15) >> 4, per = (nblk + gridDim.z - 1) / gridDim.z;
+  const int b_begin = blockIdx.z * per * 16, b_end = min(B, (blockIdx.z + 1) * per * 16);
+  if (b_begin >= b_end) return;
+  load_a(b_begin, av);
   const uint16_t* w0 = wkv_b + ((size_t)h * (kDN + kDV) + kDN + d0 + r) * kC + 8 * g;
   const uint16_t* w1 = w0 + (size_t)16 * kC;
   u32x4 bw0[16], bw1[16];
@@ -1454,8 +1459,8 @@ __global__ __launch_bounds__(64) void uproj_kernel(const uint16_t* __restrict__ 
     bw0[ks] = *(const u32x4*)(w0 + 32 * ks);
     bw1[ks] = *(const u32x4*)(w1 + 32 * ks);
   }
-  for (int b0 = 0; b0 < B; b0 += 16) {
-    if (b0 + 16 < B) load_a(b0 + 16, an);
+  for (int b0 = b_begin; b0 < b_end; b0 += 16) {
+    if (b0 + 16 < b_end) load_a(b0 + 16, an);
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) {
@@ -1567,7 +1572,10 @@ hipError_t launch_decode(const mla_params& p, const DecodeArgs& d, const CacheWr
   if (err != hipSuccess) return err;
   if (latent_out) return hipSuccess;  // the caller takes the latent output
 
-  err = launch_kernel(uproj_kernel, dim3(H, 4), dim3(64), stream, evk(3), (const uint16_t*)olat,
+  // few heads leave CUs idle: then the token blocks are split too (each share
+  // of them loads the head's W_UV slice again, from L2)
+  const int uz = std::min((B + 15) / 16, std::max(1, kTargetCUs / (4 * H)));
+  err = launch_kernel(uproj_kernel, dim3(H, 4, uz), dim3(64), stream, evk(3), (const uint16_t*)olat,
                       (const uint16_t*)d.wkv_b, (uint16_t*)d.out, B, H);
   if (err != hipSuccess) return err;
   return hipSuccess;
